@@ -1,0 +1,190 @@
+/*
+ * rba.h — ring block attention on MI355X (gfx950): the per-device step of
+ * Ring Attention and TASP, as a C ABI.
+ *
+ * What a ring step computes (TASP: Topology-aware Sequence Parallelism,
+ * abstract: each query chunk stays on its accelerator and must attend to every
+ * KV chunk, which arrive one per ring iteration; Zigzag-Ring Attention, named
+ * in its experiment highlights, is the causal load-balanced split):
+ *
+ *   For one query chunk Q and one KV chunk (K, V), exact softmax attention of
+ *   every query row against the keys of that chunk that its mask allows, as a
+ *   partial result (O_part, LSE_part).  Merging the partials of all KV chunks
+ *   with log-sum-exp weights gives exact attention over the whole sequence
+ *   (blockwise exact attention: FlashAttention and "Self-attention Does Not
+ *   Need O(n^2) Memory", both in the TASP citation map).
+ *
+ *   allowed(i, j):  NONE        always
+ *                   CAUSAL      pos(k_j) <= pos(q_i)
+ *                   DOC_CAUSAL  CAUSAL and both positions in the same packed
+ *                               document (HSAP: A Hierarchical Sequence-aware
+ *                               Parallelism for Hybrid-Context Generative
+ *                               Models, abstract and methodology: causal
+ *                               attention on packed sequences without
+ *                               attention across documents)
+ *   s_ij   = scale * <q_i, k_j>
+ *   LSE_i  = ln sum_{allowed j} exp(s_ij)         (-inf: row has no key here)
+ *   O_i    = sum_{allowed j} exp(s_ij - LSE_i) v_j (0: row has no key here)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are tokens-major and contiguous: Q, dO [sq, hq, d];
+ *     K, V [sk, hkv, d]; O / dQ [sq, hq, d]; dK, dV [sk, hkv, d];
+ *     LSE and delta [hq, sq].  Element (t, h, c) sits at (t*H + h)*d + c.
+ *   - Query head h reads KV head h / (hq / hkv) (contiguous GQA groups; GQA is
+ *     named in the TASP citation map).
+ *   - Every tensor pointer is a DEVICE pointer of the current HIP device and
+ *     must be 16-byte aligned.  Struct pointers (rba_attn, rba_segs) and
+ *     cu_seqlens_host are HOST pointers, read only during the call.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after it returns and launches on `stream` (a
+ *     hipStream_t; NULL = the legacy default stream).  Launches are
+ *     asynchronous: buffers must stay alive until the stream's work is done.
+ *   - All arguments are validated before anything is launched.  On any
+ *     negative status nothing was launched and no output was touched; the
+ *     reason is in rba_last_error().
+ *   - The library is stateless apart from a thread-local error string and is
+ *     safe to call from several threads on different streams.
+ */
+#ifndef RBA_H
+#define RBA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RBA_OK = 0,
+  RBA_STEP_EMPTY = 1,          /* not an error: no (query, key) pair of this step is
+                                  allowed; nothing was launched, outputs untouched */
+  RBA_ERR_INVALID = -1,        /* bad argument (null pointer, shape, segments, ...) */
+  RBA_ERR_UNSUPPORTED = -2,    /* valid but not implemented (d, dtype, sizes) */
+  RBA_ERR_ALIGNMENT = -3,      /* a tensor pointer is not 16-byte aligned */
+  RBA_ERR_HIP = -4             /* the HIP runtime reported an error at launch */
+} rba_status;
+
+typedef enum { RBA_BF16 = 0, RBA_F32 = 1 } rba_dtype;
+
+typedef enum { RBA_MASK_NONE = 0, RBA_MASK_CAUSAL = 1, RBA_MASK_DOC_CAUSAL = 2 } rba_mask;
+
+#define RBA_MAX_SEGS 16
+
+/*
+ * Chunk offsets: where a chunk's rows sit in the global sequence.  Row r of
+ * the chunk has global position start[s] + (r - row0(s)) where s is the
+ * segment holding row r and row0(s) = len[0] + ... + len[s-1].  A contiguous
+ * split uses one segment, the zigzag split two (pieces r and 2n-1-r), and a
+ * TASP step whose KV arrives in slices from several source ranks up to 14.
+ * Requirements: 1 <= n <= RBA_MAX_SEGS, len[s] >= 1, sum(len) equals the
+ * chunk's row count, start[s] >= 0, start[s] + len[s] <= 2^31 - 1, and the
+ * segments of one chunk do not overlap in position.
+ */
+typedef struct {
+  int32_t n;
+  int64_t start[RBA_MAX_SEGS];
+  int64_t len[RBA_MAX_SEGS];
+} rba_segs;
+
+/* Attention parameters shared by a step's forward and backward. */
+typedef struct {
+  int32_t hq;                      /* query heads, >= 1 */
+  int32_t hkv;                     /* KV heads, >= 1, divides hq */
+  int32_t d;                       /* head dimension: 64 or 128 */
+  float scale;                     /* softmax scale, finite and > 0 (usually 1/sqrt(d)) */
+  rba_dtype dtype;                 /* Q/K/V/dO element type */
+  rba_mask mask;
+  const int32_t* cu_seqlens_dev;   /* DOC_CAUSAL only: device int32[n_docs+1], ascending,
+                                      cu[0] = 0, global positions; document t is
+                                      [cu[t], cu[t+1]).  Every position of both chunks
+                                      must lie in [0, cu[n_docs]). */
+  const int32_t* cu_seqlens_host;  /* DOC_CAUSAL only, optional: the same table in host
+                                      memory.  When given, it is validated and used to
+                                      detect empty steps without a launch. */
+  int32_t n_docs;                  /* DOC_CAUSAL only: number of documents, >= 1 */
+} rba_attn;
+
+/*
+ * rba_fwd_step — one ring step of the forward pass.
+ *   q [sq, hq, d] (dtype), k and v [sk, hkv, d] (dtype); q_segs / kv_segs give
+ *   the chunks' global positions.  Writes o_part [sq, hq, d] fp32 and
+ *   lse_part [hq, sq] fp32 (natural log of the sum of exp of the scaled
+ *   scores).  Rows with no allowed key get O = 0 and LSE = -inf.
+ * Returns RBA_OK, RBA_STEP_EMPTY (host-side proof that no pair is allowed:
+ * nothing launched, outputs untouched — the caller skips the merge), or an
+ * error.  sq = 0 or sk = 0 is RBA_STEP_EMPTY.
+ * dtype RBA_BF16 supports d in {64, 128}; RBA_F32 supports d = 64.
+ */
+int rba_fwd_step(const rba_attn* a,
+                 const void* q, int64_t sq, const rba_segs* q_segs,
+                 const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                 float* o_part, float* lse_part, void* stream);
+
+/*
+ * rba_merge — LSE-weighted merge of a step's partial into the running result.
+ *   L = ln(e^{lse_acc} + e^{lse_part}),
+ *   o_acc = e^{lse_acc - L} o_acc + e^{lse_part - L} o_part,  lse_acc = L.
+ *   A side with LSE = -inf has weight 0; both -inf gives (0, -inf).
+ *   o_acc, o_part [sq, hq, d] fp32; lse_acc, lse_part [hq, sq] fp32.
+ *   o_part and lse_part may both be NULL: then the accumulator is left as it is
+ *   and only o_final is written (finalising a result that needed no merge).
+ *   o_final (nullable): also write the merged O as final_dtype (RBA_BF16 rounds
+ *   to nearest even, RBA_F32 copies) into o_final [sq, hq, d].
+ *   o_acc may not alias o_part; o_final may not alias either.
+ * d must be a multiple of 4 and at most 1024.
+ */
+int rba_merge(int64_t sq, int32_t hq, int32_t d,
+              float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+              void* o_final, int32_t final_dtype, void* stream);
+
+/*
+ * rba_bwd_preprocess — delta[h, i] = sum_c dO[i, h, c] * O[i, h, c], fp32.
+ *   o and d_o [sq, hq, d] in `dtype` (the saved forward output and its
+ *   upstream gradient); delta [hq, sq] fp32.  Run once per backward pass.
+ */
+int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t dtype,
+                       const void* o, const void* d_o, float* delta, void* stream);
+
+/*
+ * rba_bwd_step — one ring step of the backward pass (the gradient of
+ * L = sum dO * O through this step's keys).  With P_ij = exp(s_ij - lse_i)
+ * for allowed pairs (lse = the FINAL merged LSE of the forward) and
+ * dS_ij = P_ij (<dO_i, v_j> - delta_i):
+ *   dq_acc[i] += scale * sum_j dS_ij k_j            (accumulated, in/out)
+ *   dk_step[j]  = scale * sum_{i, h in group} dS_ij q_i   (overwritten)
+ *   dv_step[j]  = sum_{i, h in group} P_ij dO_i           (overwritten)
+ *   q, d_o [sq, hq, d] (dtype); k, v [sk, hkv, d] (dtype); lse, delta
+ *   [hq, sq] fp32; dq_acc [sq, hq, d] fp32; dk_step, dv_step [sk, hkv, d] fp32.
+ * On RBA_STEP_EMPTY nothing is launched: dq_acc is unchanged and dk_step /
+ * dv_step are NOT written (the step's true dK/dV are zero).  dq_acc is
+ * accumulated with fp32 atomics, so its low bits depend on scheduling.
+ * dtype RBA_BF16 only, d in {64, 128}.
+ */
+int rba_bwd_step(const rba_attn* a,
+                 const void* q, int64_t sq, const rba_segs* q_segs,
+                 const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                 const void* d_o, const float* lse, const float* delta,
+                 float* dq_acc, float* dk_step, float* dv_step, void* stream);
+
+/*
+ * rba_plan_step — host-only planning of a step (no device access).
+ * Writes into *pairs the exact number of allowed (query row, key) pairs of
+ * the step per query head (the effective work: forward 4*d flops per pair
+ * and head, backward 10*d).  For DOC_CAUSAL it needs cu_seqlens_host.
+ * Returns RBA_OK, RBA_STEP_EMPTY (pairs = 0) or an error.
+ */
+int rba_plan_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs,
+                  int64_t sk, const rba_segs* kv_segs, int64_t* pairs);
+
+/* Thread-local description of the last error on this thread ("" if none).
+ * Valid until the next rba_* call on the same thread. */
+const char* rba_last_error(void);
+
+/* Library version string, e.g. "rba 0.1.0 gfx950". */
+const char* rba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBA_H */

@@ -1,0 +1,74 @@
+"""Build the gfx950 ring block-attention library (librba.so) in-tree with hipcc.
+
+    python -m ring_sequence_parallelism_amd.build        # or build() from Python
+
+Every HIP source is compiled for gfx950 only.  Packed-fp32 VALU instructions
+are disabled for all device code (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "librba.so")
+
+SOURCES = ["rba_host.cpp", "rba_fwd.hip", "rba_merge.hip", "rba_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def _flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+        "-Wall", "-Wno-unused-function",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def _compile(src: str) -> str:
+    out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link librba.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

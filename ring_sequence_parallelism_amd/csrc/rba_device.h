@@ -1,0 +1,119 @@
+// Device-side helpers shared by the forward and backward step kernels:
+// chunk row -> global position, document starts, position ranges of row
+// ranges, and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rba_kernels.h"
+
+namespace rba {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskDoc = 2;
+constexpr int kPosNone = INT32_MIN;   // "no position": masks every key
+constexpr float kLn2 = 0.69314718055994530942f;
+// Unbounded ends of a position interval.  Positions are below 2^31, so
+// differences with these never overflow int64.
+constexpr int64_t kPosNegInf = -(int64_t(1) << 40);
+constexpr int64_t kPosPosInf = int64_t(1) << 40;
+
+// Global position of chunk row `row` (0 <= row < rows of the chunk).
+__device__ __forceinline__ int32_t row_to_pos(const SegTable& t, int32_t row) {
+  int s = 0;
+  while (s + 1 < t.n && row >= t.row0[s + 1]) ++s;
+  return t.start[s] + (row - t.row0[s]);
+}
+
+// Start of the document holding position p: the largest cu[t] <= p, t < n_docs.
+__device__ __forceinline__ int32_t doc_start(const int32_t* cu, int32_t n_docs, int32_t p) {
+  int lo = 0, hi = n_docs - 1;           // answer index in [lo, hi]
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return cu[lo];
+}
+
+// Minimum and maximum global position over chunk rows [r0, r1) (r0 < r1),
+// and whether those rows lie in a single segment.
+struct PosRange {
+  int32_t lo, hi;
+  bool single;
+};
+
+__device__ __forceinline__ PosRange pos_range(const SegTable& t, int32_t r0, int32_t r1) {
+  PosRange out{INT32_MAX, INT32_MIN, true};
+  int hits = 0;
+  for (int s = 0; s < t.n; ++s) {
+    int32_t a = max(r0, t.row0[s]);
+    int32_t b = min(r1, t.row0[s + 1]);
+    if (a < b) {
+      ++hits;
+      out.lo = min(out.lo, t.start[s] + (a - t.row0[s]));
+      out.hi = max(out.hi, t.start[s] + (b - 1 - t.row0[s]));
+    }
+  }
+  out.single = hits <= 1;
+  return out;
+}
+
+// 8 XCDs: consecutive workgroup ids are dealt round-robin to the XCDs.  Map
+// them so that every XCD works through one contiguous range of the logical
+// order, which keeps workgroups that read the same K/V head on one L2.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  constexpr int X = 8;
+  int per = n / X, rem = n % X;
+  int x = wg % X, idx = wg / X;
+  int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + idx;
+}
+
+// Tile classes.
+constexpr int kSkip = 0, kFull = 1, kPartial = 2;
+
+// Class of a key tile (positions [k.lo, k.hi], `k.single` if contiguous,
+// `ragged` if it runs past the end of the chunk) for query rows whose
+// positions lie in [q_lo, q_hi] with document starts in [ds_lo, ds_hi].
+__device__ __forceinline__ int classify(int mask, PosRange k, bool ragged,
+                                        int32_t q_lo, int32_t q_hi,
+                                        int32_t ds_lo, int32_t ds_hi, bool q_any) {
+  if (!q_any) return kSkip;
+  if (mask == kMaskNone) return ragged ? kPartial : kFull;
+  if (k.lo > q_hi) return kSkip;
+  if (mask == kMaskDoc && k.hi < ds_lo) return kSkip;
+  bool full = k.hi <= q_lo && (mask != kMaskDoc || k.lo >= ds_hi);
+  return (full && k.single && !ragged) ? kFull : kPartial;
+}
+
+// Is key position kp visible from query position qp with document start qd?
+__device__ __forceinline__ bool visible(int mask, int32_t kp, int32_t qp, int32_t qd) {
+  if (mask == kMaskNone) return true;
+  return kp <= qp && kp >= qd;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Both halves of a wave: lane l gets {v[l % 32], v[l % 32 + 32]}.
+__device__ __forceinline__ float half_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace rba

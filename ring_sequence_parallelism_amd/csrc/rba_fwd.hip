@@ -1,0 +1,488 @@
+// Forward ring step: blockwise exact softmax attention of a query chunk
+// against one KV chunk, emitting the partial output and its log-sum-exp.
+//
+// What is computed (TASP: Topology-aware Sequence Parallelism, abstract: a
+// query chunk attends to one arriving KV chunk per ring iteration; the
+// blockwise exact scheme with a running maximum and sum is that of
+// FlashAttention / FlashAttention-2, named in its citation map):
+//   for each query row i and head h, over the allowed keys j of this chunk,
+//   O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j  and  LSE_i = ln sum_j e^{s_ij}.
+//
+// gfx950 design
+//   * A workgroup is 4 waves sharing one KV head: wave w takes query head
+//     (w % hpw) of the group's heads and row block (w / hpw), so every K/V
+//     tile staged in LDS feeds 4 waves (4 GQA heads of the same rows when the
+//     group has 4 or more heads).
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: each lane owns one query column, so the row
+//     max and sum over the 32 keys of a block are 15 in-lane ops plus one
+//     v_permlane32_swap, and the fp32 accumulator of S^T converts in place to
+//     the B operand of O^T += V^T P^T (no LDS round trip for P).
+//   * Q^T stays in registers for the whole key loop.  K tiles are stored
+//     row-major in LDS; V tiles are stored transposed with the key order
+//     inside each 16-key group permuted (bits 2 and 3 swapped) so that each
+//     lane's 8 keys of a PV k-step are one 16-byte LDS read.
+//   * Key tiles outside the allowed position interval of the workgroup are
+//     never visited; inside it, each wave classifies a tile as skipped,
+//     full (no mask arithmetic) or partial (per-element mask).
+//   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
+#include "rba_device.h"
+
+namespace rba {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;  // keys per tile
+
+// Storage slot of key kk (0..63) inside a transposed V tile row.
+__device__ __forceinline__ int vt_slot(int kk) {
+  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// Setup shared by both element types: which rows/head this wave owns and the
+// allowed key interval of the workgroup.
+struct WaveTask {
+  int g, h, row0;           // kv head, query head, first row of the wave
+  int wg_row0, wg_rows;     // workgroup row range
+  bool wave_any;            // the wave has at least one valid row
+  int32_t wq_lo, wq_hi;     // wave query position range
+  int32_t wds_lo, wds_hi;   // document starts of wq_lo / wq_hi (doc mask)
+  int64_t k_lo, k_hi;       // allowed key positions for the workgroup
+};
+
+template <int QR>
+__device__ __forceinline__ WaveTask make_task(const FwdParams& p) {
+  const int wave = threadIdx.x >> 6;
+  const int logical = xcd_remap(blockIdx.x, p.n_wg);
+  const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
+  const int rg = logical % p.n_row_groups;
+  WaveTask t;
+  const int hw = wave % p.hpw, rb = wave / p.hpw;
+  t.h = hg * p.hpw + hw;
+  t.g = t.h / p.group;
+  t.wg_row0 = rg * p.rbw * QR;
+  t.wg_rows = min(p.rbw * QR, p.sq - t.wg_row0);
+  t.row0 = t.wg_row0 + rb * QR;
+  const int wr1 = min(t.row0 + QR, p.sq);
+  t.wave_any = t.row0 < wr1;
+  t.wq_lo = INT32_MAX; t.wq_hi = INT32_MIN; t.wds_lo = INT32_MIN; t.wds_hi = INT32_MIN;
+  if (t.wave_any) {
+    PosRange r = pos_range(p.qs, t.row0, wr1);
+    t.wq_lo = r.lo; t.wq_hi = r.hi;
+    if (p.mask == kMaskDoc) {
+      t.wds_lo = doc_start(p.cu, p.n_docs, r.lo);
+      t.wds_hi = doc_start(p.cu, p.n_docs, r.hi);
+    }
+  }
+  PosRange wr = pos_range(p.qs, t.wg_row0, t.wg_row0 + t.wg_rows);
+  t.k_lo = kPosNegInf; t.k_hi = kPosPosInf;
+  if (p.mask != kMaskNone) t.k_hi = wr.hi;
+  if (p.mask == kMaskDoc) t.k_lo = doc_start(p.cu, p.n_docs, wr.lo);
+  return t;
+}
+
+// Visits, in row order, every key tile that may hold an allowed key for the
+// workgroup: for each KV segment, the rows whose positions fall in
+// [k_lo, k_hi].  `body(kt)` is called once per tile.
+template <typename F>
+__device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask& t, F&& body) {
+  int next_tile = 0;
+  for (int s = 0; s < p.ks.n; ++s) {
+    const int64_t st = p.ks.start[s];
+    const int r0 = p.ks.row0[s];
+    const int64_t len = p.ks.row0[s + 1] - r0;
+    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
+    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    if (a >= b) continue;
+    const int t0 = max((int)((r0 + a) / kBN), next_tile);
+    const int t1 = (int)((r0 + b + kBN - 1) / kBN);
+    for (int kt = t0; kt < t1; ++kt) body(kt);
+    next_tile = max(next_tile, t1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16
+
+template <int D, int NQB>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int QR = 32 * NQB;
+  constexpr int KST = D + 8;     // K tile row stride (bf16 elements)
+  constexpr int VST = kBN + 8;   // V^T tile row stride
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const WaveTask t = make_task<QR>(p);
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
+
+  // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
+  bf16x8 qreg[NQB][D / 16];
+  int32_t qpos[NQB], qds[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = t.row0 + qb * 32 + col;
+    const bool ok = row < p.sq;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(
+        static_cast<const uint16_t*>(p.q) + ((size_t)(ok ? row : 0) * p.hq + t.h) * D);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 z = {};
+      qreg[qb][ks] = ok ? src[2 * ks + half] : z;
+    }
+    qpos[qb] = ok ? row_to_pos(p.qs, row) : kPosNone;
+    qds[qb] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
+  }
+
+  f32x16 oacc[NQB][D / 32];
+  float m_run[NQB], l_run[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  for_each_tile(p, t, [&](int kt) {
+    const int kr0 = kt * kBN;
+    const int kr1 = min(kr0 + kBN, p.sk);
+    __syncthreads();   // the previous tile's LDS reads are finished
+    // K tile, row-major: 16-byte chunks, consecutive threads along a row.
+#pragma unroll
+    for (int c = tid; c < kBN * D / 8; c += kThreads) {
+      const int r = c / (D / 8), c8 = c % (D / 8);
+      const int krow = kr0 + r;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (krow < p.sk)
+        val = *reinterpret_cast<const u32x4*>(kbase + ((size_t)krow * p.hkv + t.g) * D + c8 * 8);
+      *reinterpret_cast<u32x4*>(&k_lds[r * KST + c8 * 8]) = val;
+    }
+    // V tile, transposed: each unit is 4 keys x 8 dims.
+#pragma unroll
+    for (int u = tid; u < (kBN / 4) * (D / 8); u += kThreads) {
+      const int dg = u % (D / 8), kg = u / (D / 8);
+      u32x4 rows[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int krow = kr0 + 4 * kg + i;
+        rows[i] = u32x4{0u, 0u, 0u, 0u};
+        if (krow < p.sk)
+          rows[i] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)krow * p.hkv + t.g) * D + dg * 8);
+      }
+      const int slot = vt_slot(4 * kg);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
+        u32x2 lo = {(rows[0][w] & 0xffffu) | (rows[1][w] << 16), (rows[2][w] & 0xffffu) | (rows[3][w] << 16)};
+        u32x2 hi = {(rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u), (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u)};
+        *reinterpret_cast<u32x2*>(&vt_lds[(dg * 8 + 2 * w) * VST + slot]) = lo;
+        *reinterpret_cast<u32x2*>(&vt_lds[(dg * 8 + 2 * w + 1) * VST + slot]) = hi;
+      }
+    }
+    __syncthreads();
+
+    const PosRange kr = pos_range(p.ks, kr0, kr1);
+    const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    if (cls == kSkip) return;
+
+    // S^T = K Q^T for two 32-key blocks.
+    f32x16 sacc[2][NQB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) sacc[kb][qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[(kb * 32 + col) * KST + 16 * ks + 8 * half]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
+      }
+    }
+
+    if (cls == kPartial) {
+      // Key positions of this lane's 32 accumulator rows.  Every element is
+      // rewritten through a select (no conditional stores into the vectors).
+      int32_t kp[2][16];
+      if (kr.single) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+      } else {
+        for (int kb = 0; kb < 2; ++kb)
+          for (int j = 0; j < 16; ++j) {
+            const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+            kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const bool ok = kin && visible(p.mask, kp[kb][j], qpos[qb], qds[qb]);
+            sacc[kb][qb][j] = ok ? sacc[kb][qb][j] : -INFINITY;
+          }
+        }
+    }
+
+    // Online softmax (base 2) per query column, then O^T += V^T P^T.
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][qb][j]);
+      mx = half_max(mx) * p.scale_log2;
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[qb] - m_use);
+      m_run[qb] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e = fast_exp2(fmaf(sacc[kb][qb][j], p.scale_log2, -m_use));
+          sacc[kb][qb][j] = e;
+          lsum += e;
+        }
+      l_run[qb] = l_run[qb] * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+    }
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x8 pb[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = pack_bf16x2(sacc[kb][qb][8 * t2 + 2 * i], sacc[kb][qb][8 * t2 + 2 * i + 1]);
+          pb[qb] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &vt_lds[(db * 32 + col) * VST + kb * 32 + 16 * t2 + 8 * half]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
+        }
+      }
+    }
+  });
+
+  // Epilogue: O = O_acc / l, LSE = m ln 2 + ln l; rows with no key: (0, -inf).
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float l = half_sum(l_run[qb]);
+    const int row = t.row0 + qb * 32 + col;
+    const bool has = l > 0.f;
+    const float inv = has ? 1.f / l : 0.f;
+    const float lse = has ? m_run[qb] * kLn2 + __logf(l) : -INFINITY;
+    if (row < p.sq) {
+      if (half == 0) p.lse[(size_t)t.h * p.sq + row] = lse;
+      float* dst = p.o + ((size_t)row * p.hq + t.h) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4 val = {oacc[qb][db][4 * jj] * inv, oacc[qb][db][4 * jj + 1] * inv,
+                       oacc[qb][db][4 * jj + 2] * inv, oacc[qb][db][4 * jj + 3] * inv};
+          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: v_mfma_f32_32x32x2_f32, P kept in fp32.  Same structure; the V tile
+// needs no transpose because each PV k-step reads one key per lane half.
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
+  constexpr int QR = 32;
+  constexpr int KST = D + 2;   // conflict-free column reads of K
+  constexpr int VST = D + 8;   // lane halves 4 keys apart land on disjoint banks
+  __shared__ __attribute__((aligned(16))) float k_lds[kBN * KST];
+  __shared__ __attribute__((aligned(16))) float v_lds[kBN * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const WaveTask t = make_task<QR>(p);
+  const float* kbase = static_cast<const float*>(p.k);
+  const float* vbase = static_cast<const float*>(p.v);
+
+  const int row = t.row0 + col;
+  const bool row_ok = row < p.sq;
+  float qreg[D / 2];
+  {
+    const float* src = static_cast<const float*>(p.q) + ((size_t)(row_ok ? row : 0) * p.hq + t.h) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) qreg[ks] = row_ok ? src[2 * ks + half] : 0.f;
+  }
+  const int32_t qpos = row_ok ? row_to_pos(p.qs, row) : kPosNone;
+  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos) : INT32_MIN;
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for_each_tile(p, t, [&](int kt) {
+    const int kr0 = kt * kBN;
+    const int kr1 = min(kr0 + kBN, p.sk);
+    __syncthreads();
+    for (int c = tid; c < kBN * D / 4; c += kThreads) {
+      const int r = c / (D / 4), c4 = c % (D / 4);
+      const int krow = kr0 + r;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (krow < p.sk) {
+        const size_t off = ((size_t)krow * p.hkv + t.g) * D + c4 * 4;
+        kv = *reinterpret_cast<const f32x4*>(kbase + off);
+        vv = *reinterpret_cast<const f32x4*>(vbase + off);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k_lds[r * KST + c4 * 4 + i] = kv[i];
+      *reinterpret_cast<f32x4*>(&v_lds[r * VST + c4 * 4]) = vv;
+    }
+    __syncthreads();
+
+    const PosRange kr = pos_range(p.ks, kr0, kr1);
+    const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    if (cls == kSkip) return;
+
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+            k_lds[(kb * 32 + col) * KST + 2 * ks + half], qreg[ks], sacc[kb], 0, 0, 0);
+
+    if (cls == kPartial) {
+      int32_t kp[2][16];
+      if (kr.single) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+      } else {
+        for (int kb = 0; kb < 2; ++kb)
+          for (int j = 0; j < 16; ++j) {
+            const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+            kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
+          const bool ok = kin && visible(p.mask, kp[kb][j], qpos, qds);
+          sacc[kb][j] = ok ? sacc[kb][j] : -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+    mx = half_max(mx) * p.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(fmaf(sacc[kb][j], p.scale_log2, -m_use));
+        sacc[kb][j] = e;
+        lsum += e;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T: k-step j pairs key (8(j/4) + j%4) in the low lane half
+    // with the key 4 above it in the high half, exactly the keys this lane's
+    // accumulator register j holds.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(v_lds[kk * VST + db * 32 + col], sacc[kb][j],
+                                                          oacc[db], 0, 0, 0);
+      }
+  });
+
+  const float l = half_sum(l_run);
+  const bool has = l > 0.f;
+  const float inv = has ? 1.f / l : 0.f;
+  const float lse = has ? m_run * kLn2 + __logf(l) : -INFINITY;
+  if (row_ok) {
+    if (half == 0) p.lse[(size_t)t.h * p.sq + row] = lse;
+    float* dst = p.o + ((size_t)row * p.hq + t.h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 val = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                     oacc[db][4 * jj + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+constexpr int kFwdNQB = 1;
+
+int fwd_rows_per_wave(int d, int dtype_bf16) {
+  (void)d;
+  return dtype_bf16 ? 32 * kFwdNQB : 32;
+}
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
+  dim3 grid(p.n_wg), block(kThreads);
+  if (d == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB>), grid, block, 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB>), grid, block, 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s) {
+  dim3 grid(p.n_wg), block(kThreads);
+  if (d == 64)
+    hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, s, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace rba

@@ -1,0 +1,371 @@
+// C-ABI host layer of the ring block-attention library: argument validation,
+// host-side step planning (exact pair counts, empty-step detection), launch
+// geometry.  The entry points and their contracts are declared in rba.h.
+#include "rba.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "rba_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Segments
+
+struct Seg {
+  int64_t start, len, row0;
+};
+
+// Validates a chunk's segment list against its row count.  rows == 0 allows
+// n == 0.  On success fills `out` (in row order).
+int check_segs(const rba_segs* s, int64_t rows, const char* what, std::vector<Seg>& out) {
+  out.clear();
+  if (!s) return fail(RBA_ERR_INVALID, "%s: segment list is NULL", what);
+  if (s->n < 0 || s->n > RBA_MAX_SEGS)
+    return fail(RBA_ERR_INVALID, "%s: segment count %d outside [0, %d]", what, s->n, RBA_MAX_SEGS);
+  if (s->n == 0 && rows != 0) return fail(RBA_ERR_INVALID, "%s: no segments for %lld rows", what, (long long)rows);
+  int64_t total = 0;
+  for (int i = 0; i < s->n; ++i) {
+    if (s->len[i] < 1) return fail(RBA_ERR_INVALID, "%s: segment %d has length %lld", what, i, (long long)s->len[i]);
+    if (s->start[i] < 0) return fail(RBA_ERR_INVALID, "%s: segment %d starts at %lld", what, i, (long long)s->start[i]);
+    if (s->start[i] + s->len[i] > (int64_t)INT32_MAX)
+      return fail(RBA_ERR_UNSUPPORTED, "%s: segment %d reaches position %lld (limit 2^31-1)", what, i,
+                  (long long)(s->start[i] + s->len[i]));
+    out.push_back({s->start[i], s->len[i], total});
+    total += s->len[i];
+  }
+  if (total != rows)
+    return fail(RBA_ERR_INVALID, "%s: segment lengths sum to %lld, expected %lld rows", what, (long long)total,
+                (long long)rows);
+  std::vector<Seg> sorted = out;
+  std::sort(sorted.begin(), sorted.end(), [](const Seg& a, const Seg& b) { return a.start < b.start; });
+  for (size_t i = 1; i < sorted.size(); ++i)
+    if (sorted[i].start < sorted[i - 1].start + sorted[i - 1].len)
+      return fail(RBA_ERR_INVALID, "%s: segments overlap in position", what);
+  return RBA_OK;
+}
+
+rba::SegTable to_table(const std::vector<Seg>& segs) {
+  rba::SegTable t{};
+  t.n = (int32_t)segs.size();
+  int64_t r = 0;
+  for (size_t i = 0; i < segs.size(); ++i) {
+    t.start[i] = (int32_t)segs[i].start;
+    t.row0[i] = (int32_t)r;
+    r += segs[i].len;
+  }
+  t.row0[segs.size()] = (int32_t)r;
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Pair counting.  sum_{p = p0}^{p1 - 1} clamp(p - lo + 1, 0, cap): the number
+// of keys in [lo, lo + cap) at or before each position p, summed over p.
+int64_t sum_clamp(int64_t p0, int64_t p1, int64_t lo, int64_t cap) {
+  if (p1 <= p0 || cap <= 0) return 0;
+  int64_t total = 0;
+  // ramp: p in [lo, lo + cap - 1) contributes p - lo + 1
+  const int64_t r0 = std::max(p0, lo), r1 = std::min(p1, lo + cap - 1);
+  if (r1 > r0) {
+    const int64_t a = r0 - lo + 1, b = r1 - 1 - lo + 1;  // first and last term
+    total += (a + b) * (r1 - r0) / 2;
+  }
+  // plateau: p >= lo + cap - 1 contributes cap
+  const int64_t f0 = std::max(p0, lo + cap - 1);
+  if (p1 > f0) total += (p1 - f0) * cap;
+  return total;
+}
+
+struct DocTable {
+  const int32_t* cu = nullptr;
+  int32_t n = 0;
+};
+
+int check_docs(const rba_attn* a, DocTable& dt) {
+  if (!a->cu_seqlens_dev) return fail(RBA_ERR_INVALID, "document mask: cu_seqlens_dev is NULL");
+  if (a->n_docs < 1) return fail(RBA_ERR_INVALID, "document mask: n_docs = %d", a->n_docs);
+  if (a->cu_seqlens_host) {
+    const int32_t* cu = a->cu_seqlens_host;
+    if (cu[0] != 0) return fail(RBA_ERR_INVALID, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int t = 0; t < a->n_docs; ++t)
+      if (cu[t + 1] <= cu[t]) return fail(RBA_ERR_INVALID, "cu_seqlens not strictly ascending at %d", t);
+    dt.cu = cu;
+    dt.n = a->n_docs;
+  }
+  return RBA_OK;
+}
+
+int check_positions_in_docs(const std::vector<Seg>& segs, const DocTable& dt, const char* what) {
+  if (!dt.cu) return RBA_OK;
+  for (const Seg& s : segs)
+    if (s.start + s.len > dt.cu[dt.n])
+      return fail(RBA_ERR_INVALID, "%s: position %lld is past the packed buffer (%d tokens)", what,
+                  (long long)(s.start + s.len - 1), dt.cu[dt.n]);
+  return RBA_OK;
+}
+
+// Exact allowed-pair count of a step (per query head).
+int64_t count_pairs(int mask, const std::vector<Seg>& qs, const std::vector<Seg>& ks, const DocTable& dt) {
+  int64_t total = 0;
+  for (const Seg& q : qs)
+    for (const Seg& k : ks) {
+      if (mask == RBA_MASK_NONE) {
+        total += q.len * k.len;
+      } else if (mask == RBA_MASK_CAUSAL) {
+        total += sum_clamp(q.start, q.start + q.len, k.start, k.len);
+      } else {
+        // documents intersecting the query segment
+        int t = (int)(std::upper_bound(dt.cu, dt.cu + dt.n + 1, (int32_t)q.start) - dt.cu) - 1;
+        for (; t < dt.n && dt.cu[t] < q.start + q.len; ++t) {
+          const int64_t ds = dt.cu[t], de = dt.cu[t + 1];
+          const int64_t p0 = std::max(q.start, ds), p1 = std::min(q.start + q.len, de);
+          const int64_t lo = std::max(k.start, ds);
+          const int64_t cap = std::min(k.start + k.len, de) - lo;
+          total += sum_clamp(p0, p1, lo, cap);
+        }
+      }
+    }
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// Common argument checks of fwd/bwd steps.
+
+int check_attn(const rba_attn* a, bool backward) {
+  if (!a) return fail(RBA_ERR_INVALID, "attention parameters are NULL");
+  if (a->hq < 1 || a->hkv < 1) return fail(RBA_ERR_INVALID, "hq = %d, hkv = %d must be >= 1", a->hq, a->hkv);
+  if (a->hq % a->hkv) return fail(RBA_ERR_INVALID, "hq = %d is not a multiple of hkv = %d", a->hq, a->hkv);
+  if (a->d != 64 && a->d != 128) return fail(RBA_ERR_UNSUPPORTED, "head dimension %d (supported: 64, 128)", a->d);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(RBA_ERR_INVALID, "scale must be finite and > 0");
+  if (a->dtype != RBA_BF16 && a->dtype != RBA_F32) return fail(RBA_ERR_INVALID, "unknown dtype %d", (int)a->dtype);
+  if (backward && a->dtype != RBA_BF16) return fail(RBA_ERR_UNSUPPORTED, "backward step supports bf16 only");
+  if (a->mask != RBA_MASK_NONE && a->mask != RBA_MASK_CAUSAL && a->mask != RBA_MASK_DOC_CAUSAL)
+    return fail(RBA_ERR_INVALID, "unknown mask %d", (int)a->mask);
+  return RBA_OK;
+}
+
+int check_rows(int64_t rows, const char* what) {
+  if (rows < 0) return fail(RBA_ERR_INVALID, "%s: negative row count", what);
+  if (rows > (int64_t)INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "%s: %lld rows (limit 2^31-1)", what, (long long)rows);
+  return RBA_OK;
+}
+
+int check_ptr(const void* p, const char* what) {
+  if (!p) return fail(RBA_ERR_INVALID, "%s is NULL", what);
+  if (!aligned16(p)) return fail(RBA_ERR_ALIGNMENT, "%s is not 16-byte aligned", what);
+  return RBA_OK;
+}
+
+// gfx950 check, cached per device.
+int check_device() {
+  static int state[64] = {0};  // 0 unknown, 1 ok, -1 unsupported
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RBA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return RBA_OK;
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(RBA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (state[dev] < 0) return fail(RBA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return RBA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RBA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return RBA_OK;
+}
+
+// Shared preparation of a fwd or bwd step: validates, plans, fills geometry.
+struct StepPlan {
+  std::vector<Seg> qs, ks;
+  DocTable dt;
+  bool empty = false;
+};
+
+int prepare_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t sk, const rba_segs* kv_segs,
+                 bool backward, StepPlan& plan) {
+  int rc;
+  if ((rc = check_attn(a, backward))) return rc;
+  if ((rc = check_rows(sq, "query chunk"))) return rc;
+  if ((rc = check_rows(sk, "KV chunk"))) return rc;
+  if ((rc = check_segs(q_segs, sq, "query chunk", plan.qs))) return rc;
+  if ((rc = check_segs(kv_segs, sk, "KV chunk", plan.ks))) return rc;
+  if (a->mask == RBA_MASK_DOC_CAUSAL) {
+    if ((rc = check_docs(a, plan.dt))) return rc;
+    if ((rc = check_positions_in_docs(plan.qs, plan.dt, "query chunk"))) return rc;
+    if ((rc = check_positions_in_docs(plan.ks, plan.dt, "KV chunk"))) return rc;
+  }
+  plan.empty = sq == 0 || sk == 0;
+  if (!plan.empty) {
+    if (a->mask == RBA_MASK_CAUSAL) {
+      int64_t kmin = INT64_MAX, qmax = INT64_MIN;
+      for (const Seg& s : plan.ks) kmin = std::min(kmin, s.start);
+      for (const Seg& s : plan.qs) qmax = std::max(qmax, s.start + s.len - 1);
+      plan.empty = kmin > qmax;
+    } else if (a->mask == RBA_MASK_DOC_CAUSAL && plan.dt.cu) {
+      plan.empty = count_pairs(a->mask, plan.qs, plan.ks, plan.dt) == 0;
+    }
+  }
+  return RBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rba_last_error(void) { return g_err.c_str(); }
+
+const char* rba_version(void) { return "rba 0.1.0 gfx950"; }
+
+int rba_plan_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t sk, const rba_segs* kv_segs,
+                  int64_t* pairs) {
+  g_err.clear();
+  if (!pairs) return fail(RBA_ERR_INVALID, "pairs is NULL");
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
+  if (rc) return rc;
+  if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu)
+    return fail(RBA_ERR_INVALID, "planning a document-masked step needs cu_seqlens_host");
+  *pairs = (sq == 0 || sk == 0) ? 0 : count_pairs(a->mask, plan.qs, plan.ks, plan.dt);
+  return *pairs == 0 ? RBA_STEP_EMPTY : RBA_OK;
+}
+
+int rba_fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
+                 int64_t sk, const rba_segs* kv_segs, float* o_part, float* lse_part, void* stream) {
+  g_err.clear();
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o_part, "o_part")) || (rc = check_ptr(lse_part, "lse_part")))
+    return rc;
+  if (plan.empty) return RBA_STEP_EMPTY;
+  if ((rc = check_device())) return rc;
+
+  const bool bf16 = a->dtype == RBA_BF16;
+  rba::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o_part; p.lse = lse_part;
+  p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.mask = a->mask;
+  p.cu = a->mask == RBA_MASK_DOC_CAUSAL ? a->cu_seqlens_dev : nullptr;
+  p.n_docs = a->mask == RBA_MASK_DOC_CAUSAL ? a->n_docs : 0;
+  p.qs = to_table(plan.qs);
+  p.ks = to_table(plan.ks);
+  p.hpw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0 ? 2 : 1);
+  p.rbw = 4 / p.hpw;
+  const int qr = rba::fwd_rows_per_wave(a->d, bf16);
+  const int64_t rows_per_wg = (int64_t)p.rbw * qr;
+  p.n_row_groups = (int32_t)((sq + rows_per_wg - 1) / rows_per_wg);
+  p.n_head_groups = a->hq / p.hpw;
+  const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
+  if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
+  p.n_wg = (int32_t)n_wg;
+  hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
+  return hip_status(e, "forward step");
+}
+
+int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, const float* o_part,
+              const float* lse_part, void* o_final, int32_t final_dtype, void* stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_rows(sq, "merge"))) return rc;
+  if (hq < 1) return fail(RBA_ERR_INVALID, "hq = %d", hq);
+  if (d < 4 || d > 1024 || d % 4) return fail(RBA_ERR_UNSUPPORTED, "merge: d = %d (multiple of 4, <= 1024)", d);
+  if ((o_part == nullptr) != (lse_part == nullptr))
+    return fail(RBA_ERR_INVALID, "o_part and lse_part must both be given or both be NULL");
+  if (o_final && final_dtype != RBA_BF16 && final_dtype != RBA_F32)
+    return fail(RBA_ERR_INVALID, "unknown final dtype %d", final_dtype);
+  if ((rc = check_ptr(o_acc, "o_acc")) || (rc = check_ptr(lse_acc, "lse_acc"))) return rc;
+  if (o_part && ((rc = check_ptr(o_part, "o_part")) || (rc = check_ptr(lse_part, "lse_part")))) return rc;
+  if (o_final && (rc = check_ptr(o_final, "o_final"))) return rc;
+  if (o_part && (const float*)o_acc == o_part) return fail(RBA_ERR_INVALID, "o_acc aliases o_part");
+  if (o_final && (o_final == (void*)o_acc || o_final == (const void*)o_part))
+    return fail(RBA_ERR_INVALID, "o_final aliases an input");
+  if (sq == 0 || (!o_part && !o_final)) return RBA_OK;
+  if ((rc = check_device())) return rc;
+  rba::MergeParams p{};
+  p.o_acc = o_acc; p.lse_acc = lse_acc; p.o_part = o_part; p.lse_part = lse_part;
+  p.o_final = o_final; p.final_bf16 = final_dtype == RBA_BF16;
+  p.n_pairs = sq * hq; p.sq = (int32_t)sq; p.hq = hq; p.d = d;
+  return hip_status(rba::launch_merge(p, (hipStream_t)stream), "merge");
+}
+
+int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t dtype, const void* o, const void* d_o,
+                       float* delta, void* stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_rows(sq, "preprocess"))) return rc;
+  if (hq < 1) return fail(RBA_ERR_INVALID, "hq = %d", hq);
+  if (d != 64 && d != 128) return fail(RBA_ERR_UNSUPPORTED, "head dimension %d (supported: 64, 128)", d);
+  if (dtype != RBA_BF16 && dtype != RBA_F32) return fail(RBA_ERR_INVALID, "unknown dtype %d", dtype);
+  if ((rc = check_ptr(o, "o")) || (rc = check_ptr(d_o, "d_o")) || (rc = check_ptr(delta, "delta"))) return rc;
+  if (sq == 0) return RBA_OK;
+  if ((rc = check_device())) return rc;
+  rba::PrepParams p{};
+  p.o = o; p.d_o = d_o; p.delta = delta;
+  p.n_pairs = sq * hq; p.sq = (int32_t)sq; p.hq = hq; p.d = d; p.bf16 = dtype == RBA_BF16;
+  return hip_status(rba::launch_bwd_preprocess(p, (hipStream_t)stream), "backward preprocess");
+}
+
+int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
+                 int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse, const float* delta,
+                 float* dq_acc, float* dk_step, float* dv_step, void* stream) {
+  g_err.clear();
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, true, plan);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(d_o, "d_o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(delta, "delta")) ||
+      (rc = check_ptr(dq_acc, "dq_acc")) || (rc = check_ptr(dk_step, "dk_step")) ||
+      (rc = check_ptr(dv_step, "dv_step")))
+    return rc;
+  if (plan.empty) return RBA_STEP_EMPTY;
+  if ((rc = check_device())) return rc;
+  rba::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.d_o = d_o; p.lse = lse; p.delta = delta;
+  p.dq = dq_acc; p.dk = dk_step; p.dv = dv_step;
+  p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.mask = a->mask;
+  p.cu = a->mask == RBA_MASK_DOC_CAUSAL ? a->cu_seqlens_dev : nullptr;
+  p.n_docs = a->mask == RBA_MASK_DOC_CAUSAL ? a->n_docs : 0;
+  p.qs = to_table(plan.qs);
+  p.ks = to_table(plan.ks);
+  const int bk = rba::bwd_keys_per_wg(a->d);
+  p.n_key_tiles = (int32_t)((sk + bk - 1) / bk);
+  const int64_t n_wg = (int64_t)p.n_key_tiles * a->hkv;
+  if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
+  p.n_wg = (int32_t)n_wg;
+  return hip_status(rba::launch_bwd_bf16(p, a->d, (hipStream_t)stream), "backward step");
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal interface between the C-ABI host layer (rba_host.cpp) and the HIP
+// kernels.  Parameter blocks are passed to kernels by value, so everything a
+// kernel needs about a chunk's positions travels in the kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rba {
+
+constexpr int kMaxSegs = 16;
+
+// A chunk's rows mapped to global positions: rows [row0[s], row0[s+1]) hold
+// positions start[s], start[s]+1, ...  (row0[n] = number of rows).
+struct SegTable {
+  int32_t n;
+  int32_t start[kMaxSegs];
+  int32_t row0[kMaxSegs + 1];
+};
+
+// Forward step.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;            // [sq, hq, d] fp32 partial output
+  float* lse;          // [hq, sq] fp32 partial log-sum-exp
+  int32_t sq, sk, hq, hkv, group;
+  float scale_log2;    // softmax scale * log2(e): scores are exponentiated in base 2
+  int32_t mask;        // RBA_MASK_*
+  const int32_t* cu;   // device cu_seqlens (document mask)
+  int32_t n_docs;
+  SegTable qs, ks;
+  // launch geometry: each workgroup runs 4 waves; wave w takes query head
+  // (w % hpw) of its head group and row block (w / hpw) of its row group.
+  int32_t hpw;         // query heads per workgroup (1, 2 or 4)
+  int32_t rbw;         // row blocks per workgroup (4 / hpw)
+  int32_t n_row_groups;
+  int32_t n_head_groups;   // hq / hpw
+  int32_t n_wg;
+};
+
+// Backward step.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;    // [hq, sq] final log-sum-exp (natural log)
+  const float* delta;  // [hq, sq]
+  float* dq;           // [sq, hq, d] accumulated with atomics
+  float* dk;           // [sk, hkv, d] overwritten
+  float* dv;           // [sk, hkv, d] overwritten
+  int32_t sq, sk, hq, hkv, group;
+  float scale;
+  float scale_log2;
+  int32_t mask;
+  const int32_t* cu;
+  int32_t n_docs;
+  SegTable qs, ks;
+  int32_t n_key_tiles;
+  int32_t n_wg;
+};
+
+struct MergeParams {
+  float* o_acc;
+  float* lse_acc;
+  const float* o_part;   // may be null (finalise only)
+  const float* lse_part;
+  void* o_final;         // may be null
+  int32_t final_bf16;    // 1: o_final is bf16, 0: fp32
+  int64_t n_pairs;       // sq * hq
+  int32_t sq, hq, d;
+};
+
+struct PrepParams {
+  const void* o;
+  const void* d_o;
+  float* delta;
+  int64_t n_pairs;
+  int32_t sq, hq, d;
+  int32_t bf16;
+};
+
+// Launchers (defined next to their kernels).  Each returns the launch status.
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t s);
+
+// Rows of the forward workgroup tile per wave (32 * fwd_row_blocks).
+int fwd_rows_per_wave(int d, int dtype_bf16);
+// Keys per backward workgroup.
+int bwd_keys_per_wg(int d);
+
+}  // namespace rba

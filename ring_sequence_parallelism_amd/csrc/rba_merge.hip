@@ -1,0 +1,112 @@
+// LSE-weighted merge of ring-step partials, and the backward preprocess.
+//
+// Merge (blockwise exact attention, FlashAttention in the TASP citation map;
+// the merge of two partial softmax results over disjoint key sets follows from
+// the definition): with L = ln(e^{La} + e^{Lb}),
+//   O = e^{La - L} Oa + e^{Lb - L} Ob,  LSE = L,
+// and a side with LSE = -inf carrying weight 0.
+//
+// Both kernels stream memory once; they are bound by HBM bandwidth.  A
+// (row, head) pair is handled by d/4 consecutive threads, each moving one
+// 16-byte vector of every operand, so every wave reads and writes whole
+// contiguous rows.  The two LSE values of a pair are read by all its threads
+// from the same address (one request).
+#include "rba_device.h"
+
+namespace rba {
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
+  const int tpp = p.d >> 2;                       // threads per (row, head) pair
+  const int ppb = kMergeThreads / tpp;            // pairs per block per sweep
+  const int sub = threadIdx.x / tpp, c4 = threadIdx.x % tpp;
+  if (sub >= ppb) return;
+  for (int64_t pair = (int64_t)blockIdx.x * ppb + sub; pair < p.n_pairs; pair += (int64_t)gridDim.x * ppb) {
+    const int row = (int)(pair / p.hq), h = (int)(pair % p.hq);
+    const size_t li = (size_t)h * p.sq + row;
+    const size_t oi = (size_t)pair * p.d + 4 * c4;
+    f32x4 o = *reinterpret_cast<const f32x4*>(p.o_acc + oi);
+    if (p.o_part) {
+      const float la = p.lse_acc[li], lb = p.lse_part[li];
+      const float mx = fmaxf(la, lb);
+      float wa = 0.f, wb = 0.f, L = -INFINITY;
+      if (mx != -INFINITY) {
+        wa = __expf(la - mx);
+        wb = __expf(lb - mx);
+        const float s = wa + wb;
+        L = mx + __logf(s);
+        const float inv = 1.f / s;
+        wa *= inv;
+        wb *= inv;
+      }
+      const f32x4 ob = *reinterpret_cast<const f32x4*>(p.o_part + oi);
+      o = wa * o + wb * ob;
+      *reinterpret_cast<f32x4*>(p.o_acc + oi) = o;
+      if (c4 == 0) p.lse_acc[li] = L;
+    }
+    if (p.o_final) {
+      if (p.final_bf16) {
+        u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi) = o;
+      }
+    }
+  }
+}
+
+// delta[h, i] = sum_c dO[i, h, c] * O[i, h, c]
+__global__ __launch_bounds__(kMergeThreads) void bwd_preprocess_kernel(PrepParams p) {
+  const int per = p.bf16 ? 8 : 4;                 // elements per 16-byte vector
+  const int tpp = p.d / per;                      // threads per pair (power of two, <= 16)
+  const int ppb = kMergeThreads / tpp;
+  const int sub = threadIdx.x / tpp, c = threadIdx.x % tpp;
+  for (int64_t base = (int64_t)blockIdx.x * ppb; base < p.n_pairs; base += (int64_t)gridDim.x * ppb) {
+    const int64_t pair = base + sub;
+    float acc = 0.f;
+    if (pair < p.n_pairs) {
+      const size_t oi = (size_t)pair * p.d + (size_t)c * per;
+      if (p.bf16) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + oi);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.d_o) + oi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
+          acc += __uint_as_float(a[i] & 0xffff0000u) * __uint_as_float(b[i] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + oi);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.d_o) + oi);
+        acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+      }
+    }
+    // reduce over the tpp consecutive lanes of the pair
+    for (int off = tpp >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (pair < p.n_pairs && c == 0) {
+      const int row = (int)(pair / p.hq), h = (int)(pair % p.hq);
+      p.delta[(size_t)h * p.sq + row] = acc;
+    }
+  }
+}
+
+static int grid_for(int64_t n_pairs, int ppb) {
+  int64_t blocks = (n_pairs + ppb - 1) / ppb;
+  const int64_t cap = 256 * 16;   // enough resident waves to saturate HBM
+  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  const int ppb = kMergeThreads / (p.d >> 2);
+  hipLaunchKernelGGL(merge_kernel, dim3(grid_for(p.n_pairs, ppb)), dim3(kMergeThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s) {
+  const int per = p.bf16 ? 8 : 4;
+  const int ppb = kMergeThreads / (p.d / per);
+  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3(grid_for(p.n_pairs, ppb)), dim3(kMergeThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace rba

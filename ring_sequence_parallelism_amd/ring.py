@@ -1,0 +1,171 @@
+"""One rank's ring, replayed on one GPU.
+
+Ring Attention (TASP: Topology-aware Sequence Parallelism, abstract) keeps a
+rank's query chunk in place while the KV chunks of all ranks pass by, one
+per ring iteration.  Here every KV chunk is resident on the one GPU and the
+iterations are replayed in ring order: at step s rank r holds the KV chunk
+of rank (r - s) mod n.  Each step calls rba_fwd_step; the partials are
+folded with rba_merge (the last merge also writes the bf16/fp32 output), and
+steps the host proves empty launch nothing.  The backward replays the same
+steps with rba_bwd_step after one rba_bwd_preprocess.
+
+Device memory comes from torch; every arithmetic step runs in librba.so.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import rba
+from . import workloads as W
+
+_MASKS = {W.MASK_NONE: rba.RBA_MASK_NONE, W.MASK_CAUSAL: rba.RBA_MASK_CAUSAL,
+          W.MASK_DOC_CAUSAL: rba.RBA_MASK_DOC_CAUSAL}
+
+
+def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload generator output: uint16 bf16 bits -> torch.bfloat16, float32 as is."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def ring_order(r: int, n: int) -> List[int]:
+    return [(r - s) % n for s in range(n)]
+
+
+@dataclasses.dataclass
+class StepInfo:
+    src: int           # KV chunk (source rank) of this step
+    status: int        # RBA_OK or RBA_STEP_EMPTY from host planning
+    pairs: int         # allowed (query, key) pairs per query head
+
+
+class RingReplay:
+    """Device-resident inputs and buffers of one rank's ring replay."""
+
+    def __init__(self, w: W.Workload, rank: Optional[int] = None, device="cuda",
+                 kv_sources: Optional[List[int]] = None, with_grad: bool = False):
+        self.w = w
+        self.r = w.rank if rank is None else rank
+        self.device = torch.device(device)
+        self.dtype = rba.RBA_BF16 if w.dtype == "bf16" else rba.RBA_F32
+        n = w.n_ranks
+        self.order = ring_order(self.r, n)
+        srcs = sorted(set(self.order if kv_sources is None else kv_sources))
+        # inputs
+        self.q = to_device(W.gen_rank_chunk(w, W.T_Q, self.r), w.dtype, self.device)
+        self.k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in srcs}
+        self.v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in srcs}
+        self.q_segs = rba.make_segs(w.rank_segments(self.r))
+        self.kv_segs = {j: rba.make_segs(w.rank_segments(j)) for j in srcs}
+        self.cu_host = None
+        self.cu_dev = None
+        if w.mask == W.MASK_DOC_CAUSAL:
+            self.cu_host = W.gen_cu_seqlens(w)
+            self.cu_dev = torch.from_numpy(self.cu_host.astype(np.int32)).to(self.device)
+        self.attn = rba.attn_params(w.hq, w.hkv, w.d, w.scale, self.dtype, _MASKS[w.mask],
+                                    self.cu_dev, self.cu_host)
+        # host plan of every step
+        sq = self.q.shape[0]
+        self.steps: List[StepInfo] = []
+        for j in self.order:
+            if kv_sources is not None and j not in self.k:
+                continue
+            st, pairs = rba.rba_plan_step(self.attn, sq, self.q_segs, self.k[j].shape[0], self.kv_segs[j])
+            self.steps.append(StepInfo(j, st, pairs))
+        # forward buffers
+        hq, d = w.hq, w.d
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.o_acc = torch.empty((sq, hq, d), **f32)
+        self.lse_acc = torch.empty((hq, sq), **f32)
+        self.o_part = torch.empty((sq, hq, d), **f32)
+        self.lse_part = torch.empty((hq, sq), **f32)
+        out_dtype = torch.bfloat16 if self.dtype == rba.RBA_BF16 else torch.float32
+        self.o_final = torch.empty((sq, hq, d), dtype=out_dtype, device=self.device)
+        self.with_grad = with_grad
+        if with_grad:
+            self.d_o = to_device(W.gen_rank_chunk(w, W.T_DO, self.r), w.dtype, self.device)
+            self.delta = torch.empty((hq, sq), **f32)
+            self.dq = torch.empty((sq, hq, d), **f32)
+            self.dk = {s.src: torch.empty((self.k[s.src].shape[0], w.hkv, d), **f32) for s in self.steps}
+            self.dv = {s.src: torch.empty((self.k[s.src].shape[0], w.hkv, d), **f32) for s in self.steps}
+
+    # -- forward -----------------------------------------------------------
+    @property
+    def effective_pairs(self) -> int:
+        return sum(s.pairs for s in self.steps)
+
+    def fwd_flops(self) -> int:
+        """Effective forward FLOPs: 4*d per allowed pair and query head."""
+        return 4 * self.w.d * self.w.hq * self.effective_pairs
+
+    def bwd_flops(self) -> int:
+        """Effective backward FLOPs: 10*d per allowed pair and query head (5 contractions)."""
+        return 10 * self.w.d * self.w.hq * self.effective_pairs
+
+    def fwd_step(self, i: int, into_acc: bool, stream=None) -> int:
+        s = self.steps[i]
+        o, l = (self.o_acc, self.lse_acc) if into_acc else (self.o_part, self.lse_part)
+        return rba.rba_fwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                self.kv_segs[s.src], o, l, stream)
+
+    def forward(self, stream=None, on_step=None) -> torch.Tensor:
+        """Replay all steps; returns o_final (merged output in the input dtype).
+
+        ``on_step(kind, i)`` is called before each launch ("fwd" / "merge") so
+        a caller can bracket launches with events.
+        """
+        live = [i for i, s in enumerate(self.steps) if s.status == rba.RBA_OK]
+        final_dtype = rba.RBA_BF16 if self.dtype == rba.RBA_BF16 else rba.RBA_F32
+        if not live:
+            self.o_acc.zero_()
+            self.lse_acc.fill_(float("-inf"))
+            self.o_final.zero_()
+            return self.o_final
+        for n_done, i in enumerate(live):
+            first = n_done == 0
+            if on_step:
+                on_step("fwd", i)
+            st = self.fwd_step(i, into_acc=first, stream=stream)
+            assert st == rba.RBA_OK, "host plan and step status disagree"
+            if not first:
+                last = n_done == len(live) - 1
+                if on_step:
+                    on_step("merge", i)
+                rba.rba_merge(self.o_acc, self.lse_acc, self.o_part, self.lse_part,
+                              self.o_final if last else None, final_dtype, stream)
+        if len(live) == 1:
+            rba.rba_merge(self.o_acc, self.lse_acc, None, None, self.o_final, final_dtype, stream)
+        return self.o_final
+
+    # -- backward ----------------------------------------------------------
+    def backward(self, o_saved: Optional[torch.Tensor] = None, lse_saved: Optional[torch.Tensor] = None,
+                 stream=None, on_step=None):
+        """dq (fp32, accumulated over steps) and per-step dk / dv by source rank.
+
+        Uses the forward's saved output (``o_final`` by default) and merged LSE.
+        Steps the host proves empty leave their dk / dv zero.
+        """
+        assert self.with_grad
+        o_saved = self.o_final if o_saved is None else o_saved
+        lse_saved = self.lse_acc if lse_saved is None else lse_saved
+        if on_step:
+            on_step("prep", -1)
+        rba.rba_bwd_preprocess(o_saved, self.d_o, self.delta, self.dtype, stream)
+        self.dq.zero_()
+        for i, s in enumerate(self.steps):
+            if s.status != rba.RBA_OK:
+                self.dk[s.src].zero_()
+                self.dv[s.src].zero_()
+                continue
+            if on_step:
+                on_step("bwd", i)
+            st = rba.rba_bwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                  self.kv_segs[s.src], self.d_o, lse_saved, self.delta,
+                                  self.dq, self.dk[s.src], self.dv[s.src], stream)
+            assert st == rba.RBA_OK
+        return self.dq, self.dk, self.dv

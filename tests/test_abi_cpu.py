@@ -1,0 +1,199 @@
+"""C-ABI checks that need no GPU: the library loads and exports every entry
+point include/rba.h declares, argument validation rejects bad calls before
+any device work, and the host planner's exact pair counts equal the oracle's
+brute-force count of allowed pairs."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_sequence_parallelism_amd import rba
+from ring_sequence_parallelism_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rba.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rba.LIB_PATH), reason="librba.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = rba.load()
+    names = declared_functions()
+    assert set(names) == set(rba.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert rba.rba_version().startswith("rba ")
+
+
+def test_struct_layout_matches_header():
+    # rba_segs: int32 n, pad, int64[16], int64[16]; rba_attn ends with n_docs
+    assert ctypes.sizeof(rba.rba_segs) == 8 + 16 * 8 * 2
+    assert rba.rba_attn.cu_seqlens_dev.offset == 24
+    assert rba.rba_attn.n_docs.offset == 40
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails or plans only
+
+
+def _fwd(a, sq, qs, sk, ks, q=FAKE, o=FAKE):
+    lib = rba.load()
+    return lib.rba_fwd_step(ctypes.byref(a), q, sq, ctypes.byref(qs), FAKE, FAKE, sk,
+                            ctypes.byref(ks), o, FAKE, None)
+
+
+def _attn(**kw):
+    base = dict(hq=4, hkv=2, d=128, scale=0.088, dtype=rba.RBA_BF16, mask=rba.RBA_MASK_CAUSAL)
+    base.update(kw)
+    return rba.attn_params(**base)
+
+
+SEG64 = rba.make_segs([(0, 64)])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=3, hkv=2), rba.RBA_ERR_INVALID),
+    (dict(hq=0), rba.RBA_ERR_INVALID),
+    (dict(d=96), rba.RBA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), rba.RBA_ERR_INVALID),
+    (dict(scale=-1.0), rba.RBA_ERR_INVALID),
+    (dict(dtype=7), rba.RBA_ERR_INVALID),
+    (dict(mask=9), rba.RBA_ERR_INVALID),
+    (dict(mask=rba.RBA_MASK_DOC_CAUSAL), rba.RBA_ERR_INVALID),   # no cu_seqlens
+])
+def test_fwd_rejects_bad_params(kw, code):
+    assert _fwd(_attn(**kw), 64, SEG64, 64, SEG64) == code
+    assert rba.rba_last_error() != ""
+
+
+def test_fwd_rejects_bad_segments():
+    a = _attn()
+    assert _fwd(a, 64, rba.make_segs([(0, 32)]), 64, SEG64) == rba.RBA_ERR_INVALID      # sum != rows
+    assert _fwd(a, 64, rba.make_segs([(0, 40), (30, 24)]), 64, SEG64) == rba.RBA_ERR_INVALID  # overlap
+    assert _fwd(a, 64, rba.make_segs([(-5, 64)]), 64, SEG64) == rba.RBA_ERR_INVALID
+    s = rba.make_segs([(0, 64)])
+    s.n = 17
+    assert _fwd(a, 64, s, 64, SEG64) == rba.RBA_ERR_INVALID
+    assert _fwd(a, 64, rba.make_segs([(2**31 - 10, 64)]), 64, SEG64) == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_fwd_alignment_and_null():
+    a = _attn(mask=rba.RBA_MASK_NONE)
+    assert _fwd(a, 64, SEG64, 64, SEG64, q=ctypes.c_void_p(0x10008)) == rba.RBA_ERR_ALIGNMENT
+    assert _fwd(a, 64, SEG64, 64, SEG64, o=None) == rba.RBA_ERR_INVALID
+
+
+def test_empty_steps_launch_nothing():
+    a = _attn()
+    # keys entirely after the queries: causal step is empty
+    assert _fwd(a, 64, SEG64, 64, rba.make_segs([(64, 64)])) == rba.RBA_STEP_EMPTY
+    # zero rows
+    assert _fwd(a, 0, rba.make_segs([]), 64, SEG64) == rba.RBA_STEP_EMPTY
+    # document mask: keys in an earlier document
+    cu = np.array([0, 100, 200], dtype=np.int32)
+    ad = _attn(mask=rba.RBA_MASK_DOC_CAUSAL, cu_seqlens_dev=None, cu_seqlens_host=cu)
+    ad.cu_seqlens_dev = 0x20000
+    assert _fwd(ad, 50, rba.make_segs([(120, 50)]), 64, rba.make_segs([(0, 64)])) == rba.RBA_STEP_EMPTY
+    # position past the packed buffer
+    assert _fwd(ad, 50, rba.make_segs([(180, 50)]), 64, SEG64) == rba.RBA_ERR_INVALID
+
+
+def test_merge_and_preprocess_validation():
+    lib = rba.load()
+    assert lib.rba_merge(8, 2, 6, FAKE, FAKE, FAKE, FAKE, None, 0, None) == rba.RBA_ERR_UNSUPPORTED
+    assert lib.rba_merge(8, 2, 64, FAKE, FAKE, FAKE, None, None, 0, None) == rba.RBA_ERR_INVALID
+    assert lib.rba_merge(8, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == rba.RBA_ERR_INVALID  # alias
+    assert lib.rba_merge(8, 2, 64, FAKE, FAKE, None, None, None, 0, None) == rba.RBA_OK          # nothing to do
+    assert lib.rba_bwd_preprocess(8, 2, 96, 0, FAKE, FAKE, FAKE, None) == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_bwd_rejects_f32():
+    lib = rba.load()
+    a = _attn(dtype=rba.RBA_F32)
+    rc = lib.rba_bwd_step(ctypes.byref(a), FAKE, 64, ctypes.byref(SEG64), FAKE, FAKE, 64,
+                          ctypes.byref(SEG64), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == rba.RBA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Host planner vs the oracle's explicit-mask count
+
+def _positions(segs):
+    return np.concatenate([np.arange(s, s + n) for s, n in segs]) if segs else np.zeros(0, np.int64)
+
+
+def _random_segs(rng, total, rows, max_segs):
+    n = int(rng.integers(1, max_segs + 1))
+    n = min(n, rows)
+    cuts = np.sort(rng.choice(np.arange(1, rows), n - 1, replace=False)) if n > 1 else np.array([], int)
+    lens = np.diff(np.concatenate([[0], cuts, [rows]]))
+    # place the runs at disjoint random positions
+    gaps = rng.integers(0, 20, size=n)
+    starts, p = [], 0
+    order = rng.permutation(n)
+    placed = {}
+    for i in order:
+        p += int(gaps[i])
+        placed[i] = p
+        p += int(lens[i])
+    return [(placed[i], int(lens[i])) for i in range(n)]
+
+
+@pytest.mark.parametrize("mask", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_pairs_match_oracle(mask, seed):
+    rng = np.random.default_rng(1000 + 10 * mask + seed)
+    qsegs = _random_segs(rng, 0, int(rng.integers(1, 300)), 16)
+    ksegs = _random_segs(rng, 0, int(rng.integers(1, 300)), 16)
+    qpos, kpos = _positions(qsegs), _positions(ksegs)
+    end = int(max(qpos.max(), kpos.max())) + 1
+    cu = None
+    if mask == 2:
+        cuts = np.sort(rng.choice(np.arange(1, end), min(12, end - 1), replace=False))
+        cu = np.concatenate([[0], cuts, [end]]).astype(np.int32)
+    a = _attn(mask=mask, cu_seqlens_host=cu)
+    if mask == 2:
+        a.cu_seqlens_dev = 0x20000
+    st, pairs = rba.rba_plan_step(a, qpos.size, rba.make_segs(qsegs), kpos.size, rba.make_segs(ksegs))
+    want = oracle.count_pairs(qpos, kpos, mask, cu)
+    assert pairs == want
+    assert st == (rba.RBA_OK if want else rba.RBA_STEP_EMPTY)
+
+
+def test_plan_workload_totals():
+    # the 32K zigzag rank 3 and the 512K zigzag rank 0 totals over their rings
+    for key, want in (("c2", 67_110_912), ("c4", 17_179_901_952)):
+        w = W.WORKLOADS[key]
+        a = _attn(hq=w.hq, hkv=w.hkv, mask=rba.RBA_MASK_CAUSAL)
+        qs = rba.make_segs(w.rank_segments(w.rank))
+        tot = 0
+        for j in range(w.n_ranks):
+            _, p = rba.rba_plan_step(a, w.chunk_len, qs, w.chunk_len, rba.make_segs(w.rank_segments(j)))
+            tot += p
+        assert tot == want
+
+
+def test_plan_packed_docs_total():
+    w = W.WORKLOADS["c3"]
+    cu = W.gen_cu_seqlens(w)
+    a = _attn(mask=rba.RBA_MASK_DOC_CAUSAL, cu_seqlens_host=cu)
+    a.cu_seqlens_dev = 0x20000
+    tot = 0
+    nonempty = 0
+    for r in range(w.n_ranks):
+        for j in range(w.n_ranks):
+            st, p = rba.rba_plan_step(a, w.chunk_len, rba.make_segs(w.rank_segments(r)), w.chunk_len,
+                                      rba.make_segs(w.rank_segments(j)))
+            tot += p
+            nonempty += st == rba.RBA_OK
+    lens = np.diff(cu.astype(np.int64))
+    assert tot == int((lens * (lens + 1) // 2).sum())
+    assert 16 <= nonempty < 256
