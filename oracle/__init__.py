@@ -30,11 +30,11 @@ Parity pins for every function are in tests/test_oracle_*.py.  Where the
 pages are silent, the reading taken is stated at the function that takes it.
 """
 from .attn import (MASK_NONE, MASK_CAUSAL, MASK_DOC_CAUSAL, allowed_mask, attention,
-                        attention_backward, count_pairs, doc_of, merge, merge_many)
+                        attention_backward, attention_backward_sampled, count_pairs, doc_of, merge, merge_many)
 from .layouts import contiguous_positions, ring_source, zigzag_positions
 
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_DOC_CAUSAL", "allowed_mask", "attention",
-    "attention_backward", "count_pairs", "doc_of", "merge", "merge_many",
+    "attention_backward", "attention_backward_sampled", "count_pairs", "doc_of", "merge", "merge_many",
     "contiguous_positions", "ring_source", "zigzag_positions",
 ]

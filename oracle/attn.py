@@ -205,3 +205,56 @@ def attention_backward(q, k, v, do, qpos, kpos, mask: int, scale: float,
             dk[:, g, :] += scale * (ds.T @ q[i0:i1, h, :])
             dv[:, g, :] += p.T @ do_h
     return dq, dk, dv, delta, o, lse
+
+
+def attention_backward_sampled(q, k, v, do, qpos, kpos, mask: int, scale: float, cu_seqlens=None,
+                               rows=None, keys=None, heads=None, row_block: int = 512):
+    """The gradients of ``attention_backward`` on a sample of its outputs.
+
+    dq for query rows ``rows``, dk and dv for keys ``keys``, for the query
+    heads ``heads`` (dk / dv of a KV head sum only the listed heads of its
+    group, so pass whole groups to get the full dk / dv).  The softmax
+    statistics (LSE, O and delta) of every query row are computed first,
+    exactly as in the full backward; then only the sampled rows of dS and
+    the sampled columns of P and dS are formed.
+    Returns dq [len(rows), len(heads), d], dk and dv [len(keys), hkv, d]
+    (zero for KV heads with no listed query head).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    nq, hq, d, nk, hkv, group = _check_shapes(q, k, v)
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    rows = np.arange(nq) if rows is None else np.asarray(rows)
+    keys = np.arange(nk) if keys is None else np.asarray(keys)
+    heads = list(range(hq)) if heads is None else list(heads)
+    dq = np.zeros((len(rows), len(heads), d))
+    dk = np.zeros((len(keys), hkv, d))
+    dv = np.zeros((len(keys), hkv, v.shape[2]))
+    for hi, h in enumerate(heads):
+        g = h // group
+        lse = np.full(nq, -np.inf)
+        delta = np.zeros(nq)
+        for i0 in range(0, nq, row_block):
+            i1 = min(nq, i0 + row_block)
+            allow = allowed_mask(qpos[i0:i1], kpos, mask, cu_seqlens)
+            s = scale * (q[i0:i1, h, :] @ k[:, g, :].T)
+            p, lse[i0:i1] = _head_probs(s, allow)
+            delta[i0:i1] = (do[i0:i1, h, :] * (p @ v[:, g, :])).sum(axis=1)
+        # sampled rows of dS -> dq
+        allow = allowed_mask(qpos[rows], kpos, mask, cu_seqlens)
+        s = scale * (q[rows, h, :] @ k[:, g, :].T)
+        p, _ = _head_probs(s, allow)
+        ds = _score_grad(p, do[rows, h, :] @ v[:, g, :].T, delta[rows])
+        dq[:, hi, :] = scale * (ds @ k[:, g, :])
+        # sampled columns of P and dS -> dk, dv
+        allow = allowed_mask(qpos, kpos[keys], mask, cu_seqlens)
+        s = scale * (q[:, h, :] @ k[keys, g, :].T)
+        has = ~np.isneginf(lse)
+        p = np.where(allow & has[:, None], np.exp(s - np.where(has, lse, 0.0)[:, None]), 0.0)
+        ds = _score_grad(p, do[:, h, :] @ v[keys, g, :].T, delta)
+        dk[:, g, :] += scale * (ds.T @ q[:, h, :])
+        dv[:, g, :] += p.T @ do[:, h, :]
+    return dq, dk, dv

@@ -1,0 +1,176 @@
+"""GPU parity of the backward preprocess and step against the fp64 oracle.
+
+The GPU backward uses the GPU forward's saved outputs (bf16 O, fp32 merged
+LSE); the oracle uses its own fp64 forward.  dQ, dK and dV are fp32 arrays
+computed from bf16 inputs and are held to the bf16 tolerance class."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_sequence_parallelism_amd import rba
+from ring_sequence_parallelism_amd import workloads as W
+from ring_sequence_parallelism_amd.ring import RingReplay, to_device
+
+from _gpu_util import assert_close, chunk_positions, cu_or_none, full_kv_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _bf16(rng, shape):
+    bits = W.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    return bits, W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def test_preprocess():
+    _say("bwd preprocess")
+    rng = np.random.default_rng(1)
+    for d in (64, 128):
+        ob, o64 = _bf16(rng, (333, 6, d))
+        db, d64 = _bf16(rng, (333, 6, d))
+        delta = torch.empty((6, 333), device=DEV)
+        rba.rba_bwd_preprocess(to_device(ob, "bf16", DEV), to_device(db, "bf16", DEV), delta)
+        torch.cuda.synchronize()
+        want = (o64 * d64).sum(axis=2).T
+        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-4)
+
+
+def _pos(segs):
+    return np.concatenate([np.arange(s, s + n) for s, n in segs])
+
+
+STEP_CASES = [
+    # sq, sk, hq, hkv, d, qsegs, ksegs, mask
+    (200, 333, 8, 2, 128, [(150, 200)], [(0, 333)], 1),
+    (160, 130, 4, 4, 64, [(0, 60), (300, 100)], [(20, 130)], 1),
+    (96, 257, 6, 2, 128, [(257, 96)], [(0, 200), (400, 57)], 0),
+    (130, 200, 8, 2, 128, [(100, 130)], [(0, 200)], 2),
+    (1, 70, 4, 1, 128, [(69, 1)], [(0, 70)], 1),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}x{c[4]}-m{c[7]}")
+def test_step_single_chunk(case):
+    """One KV chunk holding every key: the step's gradients are the whole gradients."""
+    sq, sk, hq, hkv, d, qsegs, ksegs, mask = case
+    _say("bwd step", case)
+    rng = np.random.default_rng(sq * 7 + sk)
+    qb, q64 = _bf16(rng, (sq, hq, d))
+    kb, k64 = _bf16(rng, (sk, hkv, d))
+    vb, v64 = _bf16(rng, (sk, hkv, d))
+    dob, do64 = _bf16(rng, (sq, hq, d))
+    qpos, kpos = _pos(qsegs), _pos(ksegs)
+    cu = None
+    if mask == 2:
+        end = int(max(qpos.max(), kpos.max())) + 1
+        cu = np.array([0, 60, 150, 190, end], dtype=np.int32)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    want = oracle.attention_backward(q64, k64, v64, do64, qpos, kpos, mask, scale, cu)
+    wdq, wdk, wdv, _, wo, wlse = want
+    cu_dev = None if cu is None else torch.from_numpy(cu).to(DEV)
+    a = rba.attn_params(hq, hkv, d, scale, rba.RBA_BF16, mask, cu_dev, cu)
+    q, k, v, dO = (to_device(x, "bf16", DEV) for x in (qb, kb, vb, dob))
+    qs, ks = rba.make_segs(qsegs), rba.make_segs(ksegs)
+    # GPU forward -> saved O (bf16) and LSE, as a training step would keep them
+    o_acc = torch.empty((sq, hq, d), device=DEV)
+    lse = torch.empty((hq, sq), device=DEV)
+    o_fin = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=DEV)
+    assert rba.rba_fwd_step(a, q, qs, k, v, ks, o_acc, lse) == rba.RBA_OK
+    rba.rba_merge(o_acc, lse, None, None, o_fin, rba.RBA_BF16)
+    delta = torch.empty((hq, sq), device=DEV)
+    rba.rba_bwd_preprocess(o_fin, dO, delta)
+    dq = torch.zeros((sq, hq, d), device=DEV)
+    dk = torch.full((sk, hkv, d), float("nan"), device=DEV)
+    dv = torch.full((sk, hkv, d), float("nan"), device=DEV)
+    assert rba.rba_bwd_step(a, q, qs, k, v, ks, dO, lse, delta, dq, dk, dv) == rba.RBA_OK
+    torch.cuda.synchronize()
+    assert_close(dq.cpu().numpy(), wdq, "bf16", "dq")
+    assert_close(dk.cpu().numpy(), wdk, "bf16", "dk")
+    assert_close(dv.cpu().numpy(), wdv, "bf16", "dv")
+
+
+def _replay_grads(w, rank):
+    rr = RingReplay(w, rank, DEV, with_grad=True)
+    rr.forward()
+    dq, dk, dv = rr.backward()
+    torch.cuda.synchronize()
+    return rr, dq.cpu().numpy(), {j: t.cpu().numpy() for j, t in dk.items()}, {j: t.cpu().numpy() for j, t in dv.items()}
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_replay_zigzag_scaled(rank):
+    w = W.scaled_workload(W.WORKLOADS["c5"], 4096)
+    _say("bwd replay", w.name, "rank", rank)
+    rr, dq, dk, dv = _replay_grads(w, rank)
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, rr.r), w.dtype)
+    do64 = W.to_f64(W.gen_rank_chunk(w, W.T_DO, rr.r), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    wdq, wdk, wdv, *_ = oracle.attention_backward(q64, k64, v64, do64, chunk_positions(w, rr.r),
+                                                  np.arange(w.seq), w.mask, w.scale)
+    assert_close(dq, wdq, "bf16", "dq")
+    for j in dk:
+        kp = chunk_positions(w, j)
+        assert_close(dk[j], wdk[kp], "bf16", f"dk step src {j}")
+        assert_close(dv[j], wdv[kp], "bf16", f"dv step src {j}")
+    # invariants of the gradients summed over the ring: sum_j dK_j = 0 and
+    # sum_j dV_j = sum_i dO_i per KV head.  Per-key errors of random sign at
+    # the mean-abs tolerance accumulate like a random walk over the keys, so
+    # the sums are held to 3 * sqrt(keys) * 2e-3.
+    bound = 3 * np.sqrt(w.seq) * 2e-3
+    tot_dk = sum(dk.values()).sum(axis=0)
+    assert np.abs(tot_dk).max() < bound
+    tot_dv = sum(dv.values()).sum(axis=0)
+    want_dv = do64.reshape(do64.shape[0], w.hkv, w.hq // w.hkv, w.d).sum(axis=(0, 2))
+    assert np.abs(tot_dv - want_dv).max() < bound
+
+
+def test_replay_packed_docs_scaled():
+    w = W.scaled_workload(W.WORKLOADS["c3"], 8192, hq=8, hkv=2)
+    _say("bwd replay", w.name)
+    rr, dq, dk, dv = _replay_grads(w, 5)
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, 5), w.dtype)
+    do64 = W.to_f64(W.gen_rank_chunk(w, W.T_DO, 5), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    wdq, wdk, wdv, *_ = oracle.attention_backward(q64, k64, v64, do64, chunk_positions(w, 5),
+                                                  np.arange(w.seq), w.mask, w.scale, cu_or_none(w))
+    assert_close(dq, wdq, "bf16", "dq")
+    for j in dk:
+        kp = chunk_positions(w, j)
+        assert_close(dk[j], wdk[kp], "bf16", f"dk src {j}")
+        assert_close(dv[j], wdv[kp], "bf16", f"dv src {j}")
+
+
+def test_replay_c5_full_sampled():
+    w = W.WORKLOADS["c5"]
+    _say("bwd replay full", w.name)
+    rr, dq, dk, dv = _replay_grads(w, w.rank)
+    rows = W.gen_sampled_rows(w, 48, w.chunk_len)
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, rr.r), w.dtype)
+    do64 = W.to_f64(W.gen_rank_chunk(w, W.T_DO, rr.r), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    rng = np.random.default_rng(55)
+    keys = np.sort(rng.choice(w.seq, 64, replace=False))
+    group = w.hq // w.hkv
+    for g in (0, w.hkv - 1):
+        heads = list(range(g * group, (g + 1) * group))
+        wdq, wdk, wdv = oracle.attention_backward_sampled(
+            q64, k64, v64, do64, chunk_positions(w, rr.r), np.arange(w.seq), w.mask, w.scale,
+            rows=rows, keys=keys, heads=heads)
+        assert_close(dq[rows][:, heads], wdq, "bf16", f"dq group {g}")
+        # gather each sampled key's per-step gradient from the chunk that holds it
+        got_k = np.zeros((len(keys), w.d))
+        got_v = np.zeros((len(keys), w.d))
+        for j in dk:
+            kp = chunk_positions(w, j)
+            where = {int(p): i for i, p in enumerate(kp)}
+            for t, key in enumerate(keys):
+                if int(key) in where:
+                    got_k[t] = dk[j][where[int(key)], g]
+                    got_v[t] = dv[j][where[int(key)], g]
+        assert_close(got_k, wdk[:, g], "bf16", f"dk group {g}")
+        assert_close(got_v, wdv[:, g], "bf16", f"dv group {g}")

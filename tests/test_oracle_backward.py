@@ -141,3 +141,18 @@ def test_planted_sign_slip_is_caught(monkeypatch):
     assert _fd_check(q, k, v, do, qpos, kpos, 1, 0.6, cu)[0]
     monkeypatch.setattr(oatt, "_score_grad", lambda p, dp, delta: p * (dp + delta[:, None]))
     assert not _fd_check(q, k, v, do, qpos, kpos, 1, 0.6, cu)[0]
+
+
+@pytest.mark.parametrize("mask", [0, 1, 2])
+def test_sampled_backward_equals_full(mask):
+    rng = np.random.default_rng(90 + mask)
+    q, k, v, do, qpos, kpos, cu = _case(rng, 30, 40, 6, 2, 8, mask)
+    dq, dk, dv, *_ = oracle.attention_backward(q, k, v, do, qpos, kpos, mask, 0.4, cu)
+    rows = np.array([0, 7, 29])
+    keys = np.array([1, 2, 33, 39])
+    sdq, sdk, sdv = oracle.attention_backward_sampled(q, k, v, do, qpos, kpos, mask, 0.4, cu,
+                                                      rows=rows, keys=keys, heads=[3, 4, 5], row_block=7)
+    np.testing.assert_allclose(sdq, dq[rows][:, 3:6], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sdk[:, 1], dk[keys][:, 1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sdv[:, 1], dv[keys][:, 1], rtol=1e-12, atol=1e-13)
+    assert np.all(sdk[:, 0] == 0) and np.all(sdv[:, 0] == 0)
