@@ -158,7 +158,8 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t dtype,
  * On RBA_STEP_EMPTY nothing is launched: dq_acc is unchanged and dk_step /
  * dv_step are NOT written (the step's true dK/dV are zero).  dq_acc is
  * accumulated with fp32 atomics, so its low bits depend on scheduling.
- * dtype RBA_BF16 only, d in {64, 128}.
+ * dtype RBA_BF16 only, d in {64, 128}; dq_acc must be smaller than 4 GiB
+ * (sq * hq * d * 4 bytes), else RBA_ERR_UNSUPPORTED.
  */
 int rba_bwd_step(const rba_attn* a,
                  const void* q, int64_t sq, const rba_segs* q_segs,

@@ -3,7 +3,8 @@
     python -m ring_sequence_parallelism_amd.build        # or build() from Python
 
 Every HIP source is compiled for gfx950 only.  Packed-fp32 VALU instructions
-are disabled for all device code (-packed-fp32-ops).
+are disabled for all device code (-packed-fp32-ops), and MFMA accumulators
+are kept in VGPRs (-amdgpu-mfma-vgpr-form=1).
 """
 from __future__ import annotations
 
@@ -36,6 +37,9 @@ def _flags():
         f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
         "-Wall", "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: the softmax / dS arithmetic reads them
+        # directly instead of copying through AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]
 

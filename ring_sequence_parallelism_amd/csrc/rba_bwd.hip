@@ -14,16 +14,23 @@
 //   * A workgroup owns 128 keys of one KV head (4 waves x 32 keys).  Each wave
 //     keeps its K and V rows in registers as MFMA B operands, and its dK / dV
 //     accumulators in registers for the whole pass over every query head of
-//     the group and every query block that can see those keys.
+//     the group and every 32-row query block that can see those keys.
 //   * Scores are computed as S = Q K^T (v_mfma_f32_32x32x16_bf16) so a lane
 //     owns one key column: P and dS then feed dV += P^T dO and dK += dS^T Q as
-//     A operands straight from the accumulator registers, with Q^T and dO^T
-//     read from transposed LDS tiles whose query order inside each 16-row
-//     group is permuted (bits 2 and 3 swapped) to match the accumulator rows.
+//     A operands straight from the accumulator registers.  The matching B
+//     operands (dO and Q with the query index along k) come from the same
+//     row-major LDS tiles through the LDS transpose load, with the k order
+//     permuted to match the accumulator rows.
 //   * dQ = dS K needs the other orientation: dS goes through LDS once, and
-//     each wave computes a 32-column slice of dQ over all 128 keys against a
-//     transposed K tile staged once per workgroup, then adds it to dq_acc with
-//     fp32 atomics (consecutive lanes hit consecutive addresses).
+//     each wave computes a 32-column slice of dQ over all 128 keys (K read
+//     from a row-major LDS tile through the transpose load), then adds it to
+//     dq_acc with fp32 atomics (consecutive lanes hit consecutive addresses).
+//   * Software pipeline with one barrier per block: block i is staged into
+//     one half of double-buffered LDS tiles, then (after the barrier) the
+//     dQ of block i - 1 is computed and its atomics issued, the loads of
+//     block i + 1 are issued, and block i is computed.  Loads retire in issue
+//     order, so waiting for block i + 1's data never waits for atomics that
+//     were issued after it.
 #include "rba_device.h"
 
 namespace rba {
@@ -31,10 +38,6 @@ namespace rba {
 constexpr int kBwdThreads = 256;
 constexpr int kBK = 128;   // keys per workgroup
 constexpr int kBQ = 32;    // query rows per block
-
-__device__ __forceinline__ int q_slot(int r) {   // rows inside a 32-row block
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
 
 // End (exclusive) of the document holding position p.
 __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, int32_t p) {
@@ -46,21 +49,72 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, in
   return cu[lo + 1];
 }
 
+// Walks, for every query head of the group in turn, the 32-row query blocks
+// whose positions fall in [q_lo, q_hi] (per query segment, in row order, each
+// block once).  All fields are workgroup-uniform.
+struct QIter {
+  int hh, s, qbk, b1, next_blk;
+  bool valid;
+};
+
+__device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_t q_lo, int64_t q_hi) {
+  ++it.qbk;
+  while (it.qbk >= it.b1) {
+    ++it.s;
+    if (it.s >= p.qs.n) {
+      ++it.hh;
+      it.s = 0;
+      it.next_blk = 0;
+      if (it.hh >= p.group) {
+        it.valid = false;
+        return;
+      }
+    }
+    const int64_t st = p.qs.start[it.s];
+    const int r0 = p.qs.row0[it.s];
+    const int64_t len = p.qs.row0[it.s + 1] - r0;
+    const int64_t a = min(max(q_lo - st, (int64_t)0), len);
+    const int64_t b = min(max(q_hi - st + 1, (int64_t)0), len);
+    if (a >= b) {
+      it.qbk = 0;
+      it.b1 = 0;
+      continue;
+    }
+    const int b0 = max((int)((r0 + a) / kBQ), it.next_blk);
+    it.b1 = (int)((r0 + b + kBQ - 1) / kBQ);
+    it.next_blk = max(it.next_blk, it.b1);
+    it.qbk = b0;
+  }
+}
+
+// Class of a wave's keys (positions k, `k_bad` if ragged or split across
+// segments) against a query block (positions q).  Key-side form of the
+// document rule: key k is visible from query q iff k <= q < doc_end(k), with
+// kend_lo / kend_hi the document ends of k.lo / k.hi.
+__device__ __forceinline__ int classify_keys(int mask, PosRange k, bool k_bad, int32_t kend_lo, int32_t kend_hi,
+                                             PosRange q, bool k_any) {
+  if (!k_any) return kSkip;
+  if (mask == kMaskNone) return k_bad ? kPartial : kFull;
+  if (k.lo > q.hi) return kSkip;
+  if (mask == kMaskDoc && q.lo >= kend_hi) return kSkip;
+  const bool full = k.hi <= q.lo && (mask != kMaskDoc || q.hi < kend_lo);
+  return (full && !k_bad) ? kFull : kPartial;
+}
+
 template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
-  constexpr int QST = D + 8;       // row-major Q / dO tiles
-  constexpr int TST = kBQ + 8;     // transposed Q / dO tiles (per d row)
-  constexpr int KTST = kBK + 8;    // transposed K tile (per d row)
+  constexpr int TS = D + 16;       // row stride of the Q, dO and K tiles
   constexpr int SST = kBK + 8;     // dS tile (per query row)
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kBQ * QST];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[kBQ * QST];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * TST];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[D * TST];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * KTST];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kBQ * SST];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kBQ];
-  __shared__ __attribute__((aligned(16))) float dlt_lds[kBQ];
-  __shared__ int32_t qpos_lds[kBQ], qds_lds[kBQ];
+  constexpr int NCH = (kBQ * D / 8 + kBwdThreads - 1) / kBwdThreads;   // 16-byte chunks per thread
+  // Q, dO and dS tiles are double-buffered: block i is staged and computed in
+  // buffer i % 2 while the dQ of block i - 1 still reads dS buffer (i-1) % 2.
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][kBQ * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][kBQ * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBK * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][kBQ * SST];
+  __shared__ __attribute__((aligned(16))) float lse_lds[2][kBQ];
+  __shared__ __attribute__((aligned(16))) float dlt_lds[2][kBQ];
+  __shared__ int32_t qpos_lds[2][kBQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -95,27 +149,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
       vreg[ks] = ok ? reinterpret_cast<const bf16x8*>(vbase + off)[2 * ks + half] : z;
     }
   }
-  // Positions of this lane's key (the accumulator column it owns).
   const int my_krow = wk0 + col;
   const int32_t my_kpos = my_krow < p.sk ? row_to_pos(p.ks, my_krow) : INT32_MAX;
+  // document ends (document mask): of this lane's key and of the wave's key range
+  int32_t my_kend = INT32_MAX, wkend_lo = INT32_MAX, wkend_hi = INT32_MAX;
+  if (p.mask == kMaskDoc) {
+    if (my_krow < p.sk) my_kend = doc_end(p.cu, p.n_docs, my_kpos);
+    if (wave_any) {
+      wkend_lo = doc_end(p.cu, p.n_docs, wkr.lo);
+      wkend_hi = doc_end(p.cu, p.n_docs, wkr.hi);
+    }
+  }
 
-  // Transposed K tile for dQ = dS K: kt_lds[d][key], units of 4 keys x 8 dims.
-  for (int u = tid; u < (kBK / 4) * (D / 8); u += kBwdThreads) {
-    const int dg = u % (D / 8), kg = u / (D / 8);
-    u32x4 rows[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int krow = kr0 + 4 * kg + i;
-      rows[i] = u32x4{0u, 0u, 0u, 0u};
-      if (krow < p.sk) rows[i] = *reinterpret_cast<const u32x4*>(kbase + ((size_t)krow * p.hkv + g) * D + dg * 8);
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x2 lo = {(rows[0][w] & 0xffffu) | (rows[1][w] << 16), (rows[2][w] & 0xffffu) | (rows[3][w] << 16)};
-      u32x2 hi = {(rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u), (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(&kt_lds[(dg * 8 + 2 * w) * KTST + 4 * kg]) = lo;
-      *reinterpret_cast<u32x2*>(&kt_lds[(dg * 8 + 2 * w + 1) * KTST + 4 * kg]) = hi;
-    }
+  // Row-major K tile of the workgroup (dQ's B operand, via the transpose load).
+  for (int c = tid; c < kBK * D / 8; c += kBwdThreads) {
+    const int r = c / (D / 8), c8 = c % (D / 8);
+    const int krow = kr0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (krow < p.sk) val = *reinterpret_cast<const u32x4*>(kbase + ((size_t)krow * p.hkv + g) * D + c8 * 8);
+    *reinterpret_cast<u32x4*>(&k_lds[r * TS + c8 * 8]) = val;
   }
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
@@ -128,158 +180,167 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   if (p.mask != kMaskNone) q_lo = tkr.lo;
   if (p.mask == kMaskDoc) q_hi = (int64_t)doc_end(p.cu, p.n_docs, tkr.hi) - 1;
 
-  for (int hh = 0; hh < p.group; ++hh) {
-    const int h = g * p.group + hh;
-    int next_blk = 0;
-    for (int s = 0; s < p.qs.n; ++s) {
-      const int64_t st = p.qs.start[s];
-      const int r0 = p.qs.row0[s];
-      const int64_t len = p.qs.row0[s + 1] - r0;
-      const int64_t a = min(max(q_lo - st, (int64_t)0), len);
-      const int64_t b = min(max(q_hi - st + 1, (int64_t)0), len);
-      if (a >= b) continue;
-      const int b0 = max((int)((r0 + a) / kBQ), next_blk);
-      const int b1 = (int)((r0 + b + kBQ - 1) / kBQ);
-      next_blk = max(next_blk, b1);
-      for (int qbk = b0; qbk < b1; ++qbk) {
-        const int qr0 = qbk * kBQ;
-        const int qr1 = min(qr0 + kBQ, p.sq);
-        __syncthreads();   // previous block's LDS reads are done
-        // Q and dO rows [qr0, qr0+32) of head h: row-major and transposed.
-        {
-          const int which = tid / 128;          // 0: Q, 1: dO
-          const int u = tid % 128;
-          if (u < (kBQ / 4) * (D / 8)) {
-            const uint16_t* base = which ? dobase : qbase;
-            uint16_t* rm = which ? do_lds : q_lds;
-            uint16_t* tr = which ? dot_lds : qt_lds;
-            const int dg = u % (D / 8), rg = u / (D / 8);
-            u32x4 rows[4];
+  // Prefetch registers for one query block.  Nothing reads them before the
+  // block is staged one iteration later, so the loads stay in flight during
+  // a whole block of compute.
+  u32x4 pq[NCH], pdo[NCH];
+  float plse = 0.f, pdlt = 0.f;
+  auto fetch = [&](const QIter& b) {
+    const int h = g * p.group + b.hh;
+    const int qr0 = b.qbk * kBQ;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int qrow = qr0 + 4 * rg + i;
-              rows[i] = u32x4{0u, 0u, 0u, 0u};
-              if (qrow < p.sq)
-                rows[i] = *reinterpret_cast<const u32x4*>(base + ((size_t)qrow * p.hq + h) * D + dg * 8);
-              *reinterpret_cast<u32x4*>(&rm[(4 * rg + i) * QST + dg * 8]) = rows[i];
-            }
-            const int slot = q_slot(4 * rg);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              u32x2 lo = {(rows[0][w] & 0xffffu) | (rows[1][w] << 16), (rows[2][w] & 0xffffu) | (rows[3][w] << 16)};
-              u32x2 hi = {(rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u),
-                          (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u)};
-              *reinterpret_cast<u32x2*>(&tr[(dg * 8 + 2 * w) * TST + slot]) = lo;
-              *reinterpret_cast<u32x2*>(&tr[(dg * 8 + 2 * w + 1) * TST + slot]) = hi;
-            }
-          }
-        }
-        if (tid < kBQ) {
-          const int qrow = qr0 + tid;
-          const bool ok = qrow < p.sq;
-          const float l = ok ? p.lse[(size_t)h * p.sq + qrow] : INFINITY;
-          // log2-domain LSE; a row with no key anywhere (-inf) or past the end
-          // (+inf) yields P = 0 or is masked.
-          lse_lds[tid] = l * 1.4426950408889634f;
-          dlt_lds[tid] = ok ? p.delta[(size_t)h * p.sq + qrow] : 0.f;
-          const int32_t qp = ok ? row_to_pos(p.qs, qrow) : kPosNone;
-          qpos_lds[tid] = qp;
-          qds_lds[tid] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qp) : INT32_MIN;
-        }
-        __syncthreads();
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + kBwdThreads * i;
+      const int r = c / (D / 8), c8 = c % (D / 8);
+      const int qrow = qr0 + r;
+      pq[i] = u32x4{0u, 0u, 0u, 0u};
+      pdo[i] = u32x4{0u, 0u, 0u, 0u};
+      if (c < kBQ * D / 8 && qrow < p.sq) {
+        const size_t off = ((size_t)qrow * p.hq + h) * D + c8 * 8;
+        pq[i] = *reinterpret_cast<const u32x4*>(qbase + off);
+        pdo[i] = *reinterpret_cast<const u32x4*>(dobase + off);
+      }
+    }
+    if (tid < kBQ && qr0 + tid < p.sq) {
+      plse = p.lse[(size_t)h * p.sq + qr0 + tid];
+      pdlt = p.delta[(size_t)h * p.sq + qr0 + tid];
+    }
+  };
 
-        // Class of this wave's keys against the block's queries.
-        const PosRange qr = pos_range(p.qs, qr0, qr1);
-        int32_t ds_lo = INT32_MIN, ds_hi = INT32_MIN;
-        if (p.mask == kMaskDoc) {
-          ds_lo = doc_start(p.cu, p.n_docs, qr.lo);
-          ds_hi = doc_start(p.cu, p.n_docs, qr.hi);
-        }
-        const int cls = classify(p.mask, wkr, wave_ragged || !wkr.single, qr.lo, qr.hi, ds_lo, ds_hi, wave_any);
+  // dQ[:, slice] += scale * dS K over the 128 keys of the tile, for the block
+  // whose dS sits in buffer `buf` (rows qr0.., query head h).
+  auto dq_block = [&](int buf, int qr0, int h) {
+    constexpr int NDB = D / 32;                    // column slices
+    constexpr int KSPLIT = 4 / NDB;                // waves per slice
+    constexpr int KEYS = kBK / KSPLIT;
+    const int wd = wave % NDB, kh = wave / NDB;
+    f32x16 qacc = {};
+#pragma unroll
+    for (int ks = 0; ks < KEYS / 16; ++ks) {
+      const int key0 = kh * KEYS + 16 * ks + 8 * half;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ds_lds[buf][col * SST + key0]);
+      const bf16x8 b = tr_operand(k_lds, TS, key0, key0 + 4, wd * 32, lane);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, qacc, 0, 0, 0);
+    }
+    // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col.
+    // 32-bit element offsets from the uniform base (dq_acc is below 2^32
+    // bytes, checked on the host): one add per atomic.
+    const uint32_t row_stride = (uint32_t)p.hq * D;
+    const uint32_t base = ((uint32_t)(qr0 + 4 * half) * p.hq + h) * D + wd * 32 + col;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + (j & 3);
+      if (qr0 + 4 * half + r < p.sq) unsafeAtomicAdd(p.dq + (base + r * row_stride), qacc[j] * p.scale);
+    }
+  };
 
-        f32x16 sacc = {}, dpacc = {};
-        if (cls != kSkip) {
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&q_lds[col * QST + 16 * ks + 8 * half]);
-            const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&do_lds[col * QST + 16 * ks + 8 * half]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], sacc, 0, 0, 0);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dpacc, 0, 0, 0);
-          }
-          // P and dS in place (rows: queries 8*(j/4) + 4*half + j%4; column: my key).
-#pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4) {
-            const int qb0 = 8 * j4 + 4 * half;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[qb0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_lds[qb0]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = 4 * j4 + i;
-              // rows past the end carry LSE = +inf and get P = 0 without a mask
-              float pv = fast_exp2(fmaf(sacc[j], p.scale_log2, -l4[i]));
-              if (cls == kPartial) {
-                const int qq = qb0 + i;
-                const bool ok = my_krow < p.sk && qr0 + qq < p.sq &&
-                                visible(p.mask, my_kpos, qpos_lds[qq], qds_lds[qq]);
-                if (!ok) pv = 0.f;
-              }
-              sacc[j] = pv;
-              dpacc[j] = pv * (dpacc[j] - d4[i]);
-            }
-          }
-          // dV += P^T dO ; dK += dS^T Q  (k-step t2: queries 16*t2 + ...)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            u32x4 pw, sw;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pw[i] = pack_bf16x2(sacc[8 * t2 + 2 * i], sacc[8 * t2 + 2 * i + 1]);
-              sw[i] = pack_bf16x2(dpacc[8 * t2 + 2 * i], dpacc[8 * t2 + 2 * i + 1]);
-            }
-            const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
-            const bf16x8 sa = __builtin_bit_cast(bf16x8, sw);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const bf16x8 bdo = *reinterpret_cast<const bf16x8*>(&dot_lds[(db * 32 + col) * TST + 16 * t2 + 8 * half]);
-              const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&qt_lds[(db * 32 + col) * TST + 16 * t2 + 8 * half]);
-              dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bdo, dvacc[db], 0, 0, 0);
-              dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, bq, dkacc[db], 0, 0, 0);
-            }
-          }
-        }
-        // dS (bf16) to LDS as ds_lds[query][key]; skipped waves write zeros.
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int qq = 8 * (j >> 2) + 4 * half + (j & 3);
-          const __bf16 v = (__bf16)(cls != kSkip ? dpacc[j] : 0.f);
-          ds_lds[qq * SST + 32 * wave + col] = __builtin_bit_cast(uint16_t, v);
-        }
-        __syncthreads();
+  QIter it{0, -1, 0, 0, 0, true};
+  qiter_next(it, p, q_lo, q_hi);
+  if (it.valid) fetch(it);
+  int buf = 0;
+  int prev_qr0 = -1, prev_h = 0;      // block whose dQ is pending
 
-        // dQ[:, slice] += scale * dS K over the 128 keys of the tile.
-        {
-          constexpr int NDB = D / 32;                    // column slices
-          constexpr int KSPLIT = 4 / NDB;                // waves per slice
-          constexpr int KEYS = kBK / KSPLIT;
-          const int wd = wave % NDB, kh = wave / NDB;
-          f32x16 qacc = {};
+  while (it.valid) {
+    const int h = g * p.group + it.hh;
+    const int qr0 = it.qbk * kBQ;
+    const int qr1 = min(qr0 + kBQ, p.sq);
+    // Stage block i into buffer `buf`.  Its previous readers (block i - 2)
+    // finished before the last barrier.
 #pragma unroll
-          for (int ks = 0; ks < KEYS / 16; ++ks) {
-            const int key0 = kh * KEYS + 16 * ks + 8 * half;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ds_lds[col * SST + key0]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&kt_lds[(wd * 32 + col) * KTST + key0]);
-            qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, qacc, 0, 0, 0);
-          }
-          // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + kBwdThreads * i;
+      if (c < kBQ * D / 8) {
+        const int r = c / (D / 8), c8 = c % (D / 8);
+        *reinterpret_cast<u32x4*>(&q_lds[buf][r * TS + c8 * 8]) = pq[i];
+        *reinterpret_cast<u32x4*>(&do_lds[buf][r * TS + c8 * 8]) = pdo[i];
+      }
+    }
+    const PosRange qr = pos_range(p.qs, qr0, qr1);
+    if (tid < kBQ) {
+      const int qrow = qr0 + tid;
+      const bool ok = qrow < p.sq;
+      // log2-domain LSE; rows past the end get +inf so that P = 0
+      lse_lds[buf][tid] = ok ? plse * 1.4426950408889634f : INFINITY;
+      dlt_lds[buf][tid] = ok ? pdlt : 0.f;
+      qpos_lds[buf][tid] = !ok ? kPosNone : (qr.single ? qr.lo + tid : row_to_pos(p.qs, qrow));
+    }
+    __syncthreads();
+    // dQ of the previous block (its dS is complete in the other buffer),
+    // then the next block's loads: both stay in flight while this block runs.
+    if (prev_qr0 >= 0) dq_block(buf ^ 1, prev_qr0, prev_h);
+    QIter nx = it;
+    qiter_next(nx, p, q_lo, q_hi);
+    if (nx.valid) fetch(nx);
+
+    // Class of this wave's keys against the block's queries.
+    const int cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
+    const uint16_t* qt = q_lds[buf];
+    const uint16_t* dot = do_lds[buf];
+
+    f32x16 sacc = {}, dpacc = {};
+    if (cls != kSkip) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int qrow = qr0 + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (qrow < p.sq)
-              unsafeAtomicAdd(p.dq + ((size_t)qrow * p.hq + h) * D + wd * 32 + col, qacc[j] * p.scale);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qt[col * TS + 16 * ks + 8 * half]);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dot[col * TS + 16 * ks + 8 * half]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dpacc, 0, 0, 0);
+      }
+      // P and dS in place (rows: queries 8*(j/4) + 4*half + j%4; column: my key).
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int qb0 = 8 * j4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][qb0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_lds[buf][qb0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * j4 + i;
+          float pv = fast_exp2(fmaf(sacc[j], p.scale_log2, -l4[i]));
+          if (cls == kPartial) {
+            const int32_t qp = qpos_lds[buf][qb0 + i];
+            const bool ok = my_krow < p.sk && (p.mask == kMaskNone || (my_kpos <= qp && qp < my_kend));
+            pv = ok ? pv : 0.f;
           }
+          sacc[j] = pv;
+          dpacc[j] = pv * (dpacc[j] - d4[i]);
+        }
+      }
+      // dV += P^T dO ; dK += dS^T Q  (k-step t2: queries 16*t2 + ...)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        u32x4 pw, sw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = pack_bf16x2(sacc[8 * t2 + 2 * i], sacc[8 * t2 + 2 * i + 1]);
+          sw[i] = pack_bf16x2(dpacc[8 * t2 + 2 * i], dpacc[8 * t2 + 2 * i + 1]);
+        }
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
+        const bf16x8 sa = __builtin_bit_cast(bf16x8, sw);
+        const int rA = 16 * t2 + 4 * half, rB = rA + 8;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 bdo = tr_operand(dot, TS, rA, rB, db * 32, lane);
+          const bf16x8 bq = tr_operand(qt, TS, rA, rB, db * 32, lane);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bdo, dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, bq, dkacc[db], 0, 0, 0);
         }
       }
     }
+    // dS (bf16) to LDS as ds_lds[buf][query][key]; skipped waves write zeros.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int qq = 8 * (j >> 2) + 4 * half + (j & 3);
+      const __bf16 v = (__bf16)(cls != kSkip ? dpacc[j] : 0.f);
+      ds_lds[buf][qq * SST + 32 * wave + col] = __builtin_bit_cast(uint16_t, v);
+    }
+    prev_qr0 = qr0;
+    prev_h = h;
+    buf ^= 1;
+    it = nx;
+  }
+  if (prev_qr0 >= 0) {
+    __syncthreads();
+    dq_block(buf ^ 1, prev_qr0, prev_h);
   }
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).

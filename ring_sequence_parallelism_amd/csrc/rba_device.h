@@ -110,6 +110,34 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// MFMA operand read with the LDS transpose load (ds_read_b64_tr_b16).
+//
+// For a row-major bf16 tile X[row][col] (row stride `stride` elements), this
+// returns the operand of a 32x32x16 MFMA whose k index runs along rows and
+// whose m (or n) index is the column: lane l gets column n0 + l % 32 and the
+// 8 rows rowA + 0..3 (k-slots 0..3 of its half) and rowB + 0..3 (k-slots
+// 4..7).  The transpose load works on groups of 16 lanes: each source lane
+// supplies the address of 4 consecutive elements, and lane i of the group
+// receives element i, 16 + i, 32 + i and 48 + i of the group's 64 elements
+// in (source lane, element) order.  Source lane j of a group therefore
+// points at row (base + j / 4), column (group column + 4 * (j % 4)), and lane i
+// receives rows base..base+3 of column (group column + i).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int stride, int rowA, int rowB, int n0,
+                                             int lane) {
+  typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
+  const int j = lane & 15;
+  const int colx = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const uint16_t* pa = tile + (rowA + (j >> 2)) * stride + colx;
+  const uint16_t* pb = tile + (rowB + (j >> 2)) * stride + colx;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(pa));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(pb));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;

@@ -347,6 +347,8 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
       (rc = check_ptr(dq_acc, "dq_acc")) || (rc = check_ptr(dk_step, "dk_step")) ||
       (rc = check_ptr(dv_step, "dv_step")))
     return rc;
+  if ((int64_t)sq * a->hq * a->d * 4 >= ((int64_t)1 << 32))
+    return fail(RBA_ERR_UNSUPPORTED, "backward step: dq_acc must be smaller than 4 GiB");
   if (plan.empty) return RBA_STEP_EMPTY;
   if ((rc = check_device())) return rc;
   rba::BwdParams p{};
