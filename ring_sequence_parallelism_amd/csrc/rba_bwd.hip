@@ -11,10 +11,15 @@
 // summing dK / dV over the query heads that share a KV head (GQA).
 //
 // gfx950 design
-//   * A workgroup owns 128 keys of one KV head (4 waves x 32 keys).  Each wave
-//     keeps its K and V rows in registers as MFMA B operands, and its dK / dV
-//     accumulators in registers for the whole pass over every query head of
-//     the group and every 32-row query block that can see those keys.
+//   * A workgroup owns 128 keys of one KV head and one query head of its
+//     group (4 waves x 32 keys).  Each wave keeps its K and V rows in
+//     registers as MFMA B operands, and its dK / dV accumulators in registers
+//     for the whole pass over the 32-row query blocks that can see those
+//     keys.  Splitting the group's query heads over workgroups balances the
+//     causal work (low key tiles see every query block); the group's partial
+//     dK / dV are summed with fp32 atomics into zeroed outputs.  Workgroups
+//     are ordered KV head, key tile, query head, so the heavier low key tiles
+//     are dispatched first on every XCD.
 //   * Scores are computed as S = Q K^T (v_mfma_f32_32x32x16_bf16) so a lane
 //     owns one key column: P and dS then feed dV += P^T dO and dK += dS^T Q as
 //     A operands straight from the accumulator registers.  The matching B
@@ -49,11 +54,11 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, in
   return cu[lo + 1];
 }
 
-// Walks, for every query head of the group in turn, the 32-row query blocks
-// whose positions fall in [q_lo, q_hi] (per query segment, in row order, each
-// block once).  All fields are workgroup-uniform.
+// Walks the 32-row query blocks whose positions fall in [q_lo, q_hi] (per
+// query segment, in row order, each block once).  All fields are
+// workgroup-uniform.
 struct QIter {
-  int hh, s, qbk, b1, next_blk;
+  int s, qbk, b1, next_blk;
   bool valid;
 };
 
@@ -62,13 +67,8 @@ __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_
   while (it.qbk >= it.b1) {
     ++it.s;
     if (it.s >= p.qs.n) {
-      ++it.hh;
-      it.s = 0;
-      it.next_blk = 0;
-      if (it.hh >= p.group) {
-        it.valid = false;
-        return;
-      }
+      it.valid = false;
+      return;
     }
     const int64_t st = p.qs.start[it.s];
     const int r0 = p.qs.row0[it.s];
@@ -119,8 +119,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, p.n_wg);
-  const int g = logical / p.n_key_tiles;
-  const int kt = logical % p.n_key_tiles;
+  const int g = logical / (p.n_key_tiles * p.group);
+  const int kt = (logical / p.group) % p.n_key_tiles;
+  const int h = g * p.group + logical % p.group;   // the query head of this workgroup
   const int kr0 = kt * kBK;
   const int kr1 = min(kr0 + kBK, p.sk);
   const uint16_t* qbase = static_cast<const uint16_t*>(p.q);
@@ -186,7 +187,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   u32x4 pq[NCH], pdo[NCH];
   float plse = 0.f, pdlt = 0.f;
   auto fetch = [&](const QIter& b) {
-    const int h = g * p.group + b.hh;
     const int qr0 = b.qbk * kBQ;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   };
 
   // dQ[:, slice] += scale * dS K over the 128 keys of the tile, for the block
-  // whose dS sits in buffer `buf` (rows qr0.., query head h).
-  auto dq_block = [&](int buf, int qr0, int h) {
+  // whose dS sits in buffer `buf` (rows qr0..).
+  auto dq_block = [&](int buf, int qr0) {
     constexpr int NDB = D / 32;                    // column slices
     constexpr int KSPLIT = 4 / NDB;                // waves per slice
     constexpr int KEYS = kBK / KSPLIT;
@@ -234,14 +234,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     }
   };
 
-  QIter it{0, -1, 0, 0, 0, true};
+  QIter it{-1, 0, 0, 0, true};
   qiter_next(it, p, q_lo, q_hi);
   if (it.valid) fetch(it);
   int buf = 0;
-  int prev_qr0 = -1, prev_h = 0;      // block whose dQ is pending
+  int prev_qr0 = -1;      // block whose dQ is pending
 
   while (it.valid) {
-    const int h = g * p.group + it.hh;
     const int qr0 = it.qbk * kBQ;
     const int qr1 = min(qr0 + kBQ, p.sq);
     // Stage block i into buffer `buf`.  Its previous readers (block i - 2)
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     __syncthreads();
     // dQ of the previous block (its dS is complete in the other buffer),
     // then the next block's loads: both stay in flight while this block runs.
-    if (prev_qr0 >= 0) dq_block(buf ^ 1, prev_qr0, prev_h);
+    if (prev_qr0 >= 0) dq_block(buf ^ 1, prev_qr0);
     QIter nx = it;
     qiter_next(nx, p, q_lo, q_hi);
     if (nx.valid) fetch(nx);
@@ -334,27 +333,52 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
       ds_lds[buf][qq * SST + 32 * wave + col] = __builtin_bit_cast(uint16_t, v);
     }
     prev_qr0 = qr0;
-    prev_h = h;
     buf ^= 1;
     it = nx;
   }
   if (prev_qr0 >= 0) {
     __syncthreads();
-    dq_block(buf ^ 1, prev_qr0, prev_h);
+    dq_block(buf ^ 1, prev_qr0);
   }
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).
+  // With one query head per KV head the workgroup owns its keys' gradients
+  // and stores them; otherwise the group's workgroups add into zeroed outputs.
+  if (!wave_any) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int krow = wk0 + 8 * (j >> 2) + 4 * half + (j & 3);
       if (krow < p.sk) {
-        const size_t off = ((size_t)krow * p.hkv + g) * D + db * 32 + col;
-        p.dk[off] = dkacc[db][j] * p.scale;
-        p.dv[off] = dvacc[db][j];
+        float* dkp = p.dk + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
+        float* dvp = p.dv + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
+        if (p.group == 1) {
+          *dkp = dkacc[db][j] * p.scale;
+          *dvp = dvacc[db][j];
+        } else {
+          unsafeAtomicAdd(dkp, dkacc[db][j] * p.scale);
+          unsafeAtomicAdd(dvp, dvacc[db][j]);
+        }
       }
     }
+}
+
+// Zero two fp32 arrays of n elements (n a multiple of 4, 16-byte aligned).
+__global__ __launch_bounds__(256) void zero2_kernel(float* a, float* b, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    reinterpret_cast<f32x4*>(a)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    reinterpret_cast<f32x4*>(b)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+hipError_t launch_zero_f32(float* a, float* b, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, b, n4);
+  return hipGetLastError();
 }
 
 int bwd_keys_per_wg(int d) {

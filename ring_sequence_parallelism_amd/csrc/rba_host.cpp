@@ -364,9 +364,14 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
   p.ks = to_table(plan.ks);
   const int bk = rba::bwd_keys_per_wg(a->d);
   p.n_key_tiles = (int32_t)((sk + bk - 1) / bk);
-  const int64_t n_wg = (int64_t)p.n_key_tiles * a->hkv;
+  const int64_t n_wg = (int64_t)p.n_key_tiles * a->hq;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
+  if (p.group > 1) {
+    // the group's workgroups add their partial dK / dV into zeroed outputs
+    hipError_t e = rba::launch_zero_f32(dk_step, dv_step, sk * a->hkv * a->d, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "backward zero fill");
+  }
   return hip_status(rba::launch_bwd_bf16(p, a->d, (hipStream_t)stream), "backward step");
 }
 

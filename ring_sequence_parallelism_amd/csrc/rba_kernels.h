@@ -59,7 +59,7 @@ struct BwdParams {
   int32_t n_docs;
   SegTable qs, ks;
   int32_t n_key_tiles;
-  int32_t n_wg;
+  int32_t n_wg;      // n_key_tiles * hkv * group: one workgroup per (key tile, query head)
 };
 
 struct MergeParams {
@@ -88,6 +88,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_zero_f32(float* a, float* b, int64_t n, hipStream_t s);
 
 // Rows of the forward workgroup tile per wave (32 * fwd_row_blocks).
 int fwd_rows_per_wave(int d, int dtype_bf16);
