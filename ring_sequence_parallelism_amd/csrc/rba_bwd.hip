@@ -213,24 +213,39 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     constexpr int NDB = D / 32;                    // column slices
     constexpr int KSPLIT = 4 / NDB;                // waves per slice
     constexpr int KEYS = kBK / KSPLIT;
+    constexpr int NKS = KEYS / 16;
     const int wd = wave % NDB, kh = wave / NDB;
-    f32x16 qacc = {};
+    // all operands first, then two independent accumulation chains
+    bf16x8 a[NKS], b[NKS];
 #pragma unroll
-    for (int ks = 0; ks < KEYS / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       const int key0 = kh * KEYS + 16 * ks + 8 * half;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ds_lds[buf][col * SST + key0]);
-      const bf16x8 b = tr_operand(k_lds, TS, key0, key0 + 4, wd * 32, lane);
-      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, qacc, 0, 0, 0);
+      a[ks] = *reinterpret_cast<const bf16x8*>(&ds_lds[buf][col * SST + key0]);
+      b[ks] = tr_operand(k_lds, TS, key0, key0 + 4, wd * 32, lane);
+    }
+    f32x16 q0 = {}, q1 = {};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks += 2) {
+      q0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], q0, 0, 0, 0);
+      q1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks + 1], b[ks + 1], q1, 0, 0, 0);
     }
     // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col.
     // 32-bit element offsets from the uniform base (dq_acc is below 2^32
-    // bytes, checked on the host): one add per atomic.
+    // bytes, checked on the host); the row offsets are scalar multiples.
     const uint32_t row_stride = (uint32_t)p.hq * D;
-    const uint32_t base = ((uint32_t)(qr0 + 4 * half) * p.hq + h) * D + wd * 32 + col;
+    float* base = p.dq + (((uint32_t)(qr0 + 4 * half) * p.hq + h) * D + wd * 32 + col);
+    if (qr0 + kBQ <= p.sq) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 8 * (j >> 2) + (j & 3);
-      if (qr0 + 4 * half + r < p.sq) unsafeAtomicAdd(p.dq + (base + r * row_stride), qacc[j] * p.scale);
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t r = 8 * (j >> 2) + (j & 3);
+        unsafeAtomicAdd(base + r * row_stride, (q0[j] + q1[j]) * p.scale);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t r = 8 * (j >> 2) + (j & 3);
+        if (qr0 + 4 * half + (int)r < p.sq) unsafeAtomicAdd(base + r * row_stride, (q0[j] + q1[j]) * p.scale);
+      }
     }
   };
 

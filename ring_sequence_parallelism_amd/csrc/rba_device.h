@@ -138,6 +138,41 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int stride, i
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// XOR swizzle of 16-byte chunks inside a row of a bf16 tile that has no
+// padding (rows of CPR chunks, CPR = 16 for d = 128, 8 for d = 64): chunk c of
+// row r is stored at chunk position c ^ tile_swz(r).  Rows r and r + 1..15
+// (CPR = 16) map a given chunk to distinct positions, so 16 lanes reading the
+// same chunk of 16 rows hit distinct banks; the four rows of a transpose
+// load see distinct chunk pairs.
+template <int CPR>
+__device__ __forceinline__ int tile_swz(int r) {
+  return CPR == 16 ? ((2 * (r & 7)) | ((r >> 3) & 1)) : ((2 * (r & 3)) | ((r >> 2) & 1));
+}
+
+// tr_operand for a swizzled, unpadded tile (base = byte address of row 0).
+template <int CPR>
+__device__ __forceinline__ bf16x8 tr_operand_swz(const char* base, int rowA, int rowB, int n0, int lane) {
+  typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
+  const int j = lane & 15;
+  const int colx = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);   // element column
+  const int c = colx >> 3, within = (colx & 7) * 2;
+  const int ra = rowA + (j >> 2), rb = rowB + (j >> 2);
+  const char* pa = base + ra * (CPR * 16) + ((c ^ tile_swz<CPR>(ra)) << 4) + within;
+  const char* pb = base + rb * (CPR * 16) + ((c ^ tile_swz<CPR>(rb)) << 4) + within;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(pa));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(pb));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's data lands
+// at lds_wave_base + 16 * l (lds_wave_base must be the same for the wave).
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gptr,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;

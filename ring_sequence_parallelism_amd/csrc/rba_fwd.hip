@@ -18,14 +18,17 @@
 //     max and sum over the 32 keys of a block are 15 in-lane ops plus one
 //     v_permlane32_swap, and the fp32 accumulator of S^T converts in place to
 //     the B operand of O^T += V^T P^T (no LDS round trip for P).
-//   * Q^T stays in registers for the whole key loop.  K tiles are stored
-//     row-major in LDS; V tiles are stored transposed with the key order
-//     inside each 16-key group permuted (bits 2 and 3 swapped) so that each
-//     lane's 8 keys of a PV k-step are one 16-byte LDS read.
+//   * Q^T stays in registers for the whole key loop.  K and V tiles stream
+//     from HBM straight into double-buffered LDS (global_load_lds, 16 bytes
+//     per lane, no register staging) while the previous tile is computed;
+//     rows are unpadded with an XOR swizzle of their 16-byte chunks.  V is
+//     read as the A operand of PV through the LDS transpose load, in the
+//     key order the P^T accumulator rows imply.  One barrier per tile.
 //   * Key tiles outside the allowed position interval of the workgroup are
 //     never visited; inside it, each wave classifies a tile as skipped,
 //     full (no mask arithmetic) or partial (per-element mask).
-//   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
+//   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score,
+//     and a lazy running maximum that rarely rescales O.
 #include "rba_device.h"
 
 namespace rba {
@@ -104,15 +107,50 @@ __device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask
 // ---------------------------------------------------------------------------
 // bf16
 
+// Iterator over the key tiles for_each_tile visits (same order), so that the
+// next tile's loads can be issued before the current tile is computed.
+struct TileIter {
+  int s, kt, t1, next_tile;
+  bool valid;
+};
+
+__device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, const WaveTask& t) {
+  ++it.kt;
+  while (it.kt >= it.t1) {
+    ++it.s;
+    if (it.s >= p.ks.n) {
+      it.valid = false;
+      return;
+    }
+    const int64_t st = p.ks.start[it.s];
+    const int r0 = p.ks.row0[it.s];
+    const int64_t len = p.ks.row0[it.s + 1] - r0;
+    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
+    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    if (a >= b) {
+      it.kt = 0;
+      it.t1 = 0;
+      continue;
+    }
+    it.kt = max((int)((r0 + a) / kBN), it.next_tile);
+    it.t1 = (int)((r0 + b + kBN - 1) / kBN);
+    it.next_tile = max(it.next_tile, it.t1);
+  }
+}
+
 template <int D, int NQB>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int QR = 32 * NQB;
-  constexpr int KST = D + 8;     // K tile row stride (bf16 elements)
-  constexpr int VST = kBN + 8;   // V^T tile row stride
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RB = D * 2;                  // bytes per row (no padding: swizzled)
+  constexpr int TILE = kBN * RB;             // bytes per K or V tile
+  constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
+  constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;   // per wave per tensor per tile
+  // [buffer][K, V] tiles, double-buffered: tile t is computed from buffer t % 2
+  // while tile t + 1 streams into the other one.
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const WaveTask t = make_task<QR>(p);
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
@@ -136,6 +174,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     qds[qb] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
   }
 
+  // Issue the direct-to-LDS loads of key tile kt into buffer b.  Lane l of
+  // load i writes chunk position l % CPR of tile row (first row + l / CPR);
+  // it fetches the global chunk that the swizzle stores there.  Rows past the
+  // end of the chunk re-read the last row (finite values; masked out).
+  auto issue = [&](int kt, int b) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
+      const int cp = lane % CPR;
+      const int c = cp ^ tile_swz<CPR>(r);
+      const int krow = min(kt * kBN + r, p.sk - 1);
+      const size_t off = ((size_t)krow * p.hkv + t.g) * D + c * 8;
+      char* dst = &lds[b][0][(wave * LOADS + i) * 64 * 16];
+      load_lds16(kbase + off, dst);
+      load_lds16(vbase + off, dst + TILE);
+    }
+  };
+
   f32x16 oacc[NQB][D / 32];
   float m_run[NQB], l_run[NQB];
 #pragma unroll
@@ -146,145 +202,138 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  for_each_tile(p, t, [&](int kt) {
+  TileIter it{-1, 0, 0, 0, true};
+  tile_next(it, p, t);
+  if (it.valid) issue(it.kt, 0);
+  int buf = 0;
+  while (it.valid) {
+    const int kt = it.kt;
     const int kr0 = kt * kBN;
     const int kr1 = min(kr0 + kBN, p.sk);
-    __syncthreads();   // the previous tile's LDS reads are finished
-    // K tile, row-major: 16-byte chunks, consecutive threads along a row.
-#pragma unroll
-    for (int c = tid; c < kBN * D / 8; c += kThreads) {
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      const int krow = kr0 + r;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (krow < p.sk)
-        val = *reinterpret_cast<const u32x4*>(kbase + ((size_t)krow * p.hkv + t.g) * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(&k_lds[r * KST + c8 * 8]) = val;
-    }
-    // V tile, transposed: each unit is 4 keys x 8 dims.
-#pragma unroll
-    for (int u = tid; u < (kBN / 4) * (D / 8); u += kThreads) {
-      const int dg = u % (D / 8), kg = u / (D / 8);
-      u32x4 rows[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int krow = kr0 + 4 * kg + i;
-        rows[i] = u32x4{0u, 0u, 0u, 0u};
-        if (krow < p.sk)
-          rows[i] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)krow * p.hkv + t.g) * D + dg * 8);
-      }
-      const int slot = vt_slot(4 * kg);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
-        u32x2 lo = {(rows[0][w] & 0xffffu) | (rows[1][w] << 16), (rows[2][w] & 0xffffu) | (rows[3][w] << 16)};
-        u32x2 hi = {(rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u), (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(&vt_lds[(dg * 8 + 2 * w) * VST + slot]) = lo;
-        *reinterpret_cast<u32x2*>(&vt_lds[(dg * 8 + 2 * w + 1) * VST + slot]) = hi;
-      }
-    }
+    // This wave's loads of tile kt have landed; after the barrier every
+    // wave's have, and every wave is done with the other buffer.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    TileIter nx = it;
+    tile_next(nx, p, t);
+    if (nx.valid) issue(nx.kt, buf ^ 1);
 
     const PosRange kr = pos_range(p.ks, kr0, kr1);
     const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
-    if (cls == kSkip) return;
-
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16 sacc[2][NQB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) sacc[kb][qb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[(kb * 32 + col) * KST + 16 * ks + 8 * half]);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
-      }
-    }
-
-    if (cls == kPartial) {
-      // Key positions of this lane's 32 accumulator rows.  Every element is
-      // rewritten through a select (no conditional stores into the vectors).
-      int32_t kp[2][16];
-      if (kr.single) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-      } else {
-        for (int kb = 0; kb < 2; ++kb)
-          for (int j = 0; j < 16; ++j) {
-            const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-            kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
-          }
-      }
+    if (cls != kSkip) {
+      const char* kt_lds = lds[buf][0];
+      const char* vt_lds = lds[buf][1];
+      // S^T = K Q^T for two 32-key blocks.
+      f32x16 sacc[2][NQB];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
+        for (int qb = 0; qb < NQB; ++qb) sacc[kb][qb] = f32x16{};
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const bool ok = kin && visible(p.mask, kp[kb][j], qpos[qb], qds[qb]);
-            sacc[kb][qb][j] = ok ? sacc[kb][qb][j] : -INFINITY;
-          }
-        }
-    }
-
-    // Online softmax (base 2) per query column, then O^T += V^T P^T.
+      for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][qb][j]);
-      mx = half_max(mx) * p.scale_log2;
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[qb] - m_use);
-      m_run[qb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = fast_exp2(fmaf(sacc[kb][qb][j], p.scale_log2, -m_use));
-          sacc[kb][qb][j] = e;
-          lsum += e;
-        }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
-    }
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x8 pb[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          u32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] = pack_bf16x2(sacc[kb][qb][8 * t2 + 2 * i], sacc[kb][qb][8 * t2 + 2 * i + 1]);
-          pb[qb] = __builtin_bit_cast(bf16x8, w);
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = kb * 32 + col;
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &vt_lds[(db * 32 + col) * VST + kb * 32 + 16 * t2 + 8 * half]);
+              kt_lds + r * RB + (((2 * ks + half) ^ tile_swz<CPR>(r)) << 4));
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
+            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
+        }
+      }
+
+      if (cls == kPartial) {
+        // Key positions of this lane's 32 accumulator rows.  Every element is
+        // rewritten through a select (no conditional stores into the vectors).
+        int32_t kp[2][16];
+        if (kr.single) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        } else {
+          for (int kb = 0; kb < 2; ++kb)
+            for (int j = 0; j < 16; ++j) {
+              const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+              kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+              const bool ok = kin && visible(p.mask, kp[kb][j], qpos[qb], qds[qb]);
+              sacc[kb][qb][j] = ok ? sacc[kb][qb][j] : -INFINITY;
+            }
+          }
+      }
+
+      // Online softmax (base 2) per query column with a lazy maximum: the
+      // running maximum only moves (and O, l are only rescaled) when some
+      // lane's tile maximum exceeds it by more than 2^8, so P stays below
+      // 256 and most tiles skip the rescale.
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][qb][j]);
+        mx = half_max(mx) * p.scale_log2;
+        if (__any(mx > m_run[qb] + 8.f)) {
+          const float m_new = fmaxf(m_run[qb], mx);
+          const float alpha = fast_exp2(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+        }
+        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float e = fast_exp2(fmaf(sacc[kb][qb][j], p.scale_log2, -m_use));
+            sacc[kb][qb][j] = e;
+            lsum += e;
+          }
+        l_run[qb] += lsum;
+      }
+
+      // O^T += V^T P^T.  The k-slot of P^T register j maps to key
+      // 16*t2 + 8*(i/4) + 4*half + i%4; the transpose load reads V rows in
+      // that order straight from the row-major tile.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x8 pb[NQB];
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[i] = pack_bf16x2(sacc[kb][qb][8 * t2 + 2 * i], sacc[kb][qb][8 * t2 + 2 * i + 1]);
+            pb[qb] = __builtin_bit_cast(bf16x8, w);
+          }
+          const int rA = kb * 32 + 16 * t2 + 4 * half;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = tr_operand_swz<CPR>(vt_lds, rA, rA + 8, db * 32, lane);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
+          }
         }
       }
     }
-  });
+    buf ^= 1;
+    it = nx;
+  }
 
   // Epilogue: O = O_acc / l, LSE = m ln 2 + ln l; rows with no key: (0, -inf).
 #pragma unroll
