@@ -4,7 +4,8 @@
 A bench "step" is one pass of the whole hot path over one batch of
 synthetic input: the forward ring replay (8 rba_fwd_step launches folded
 with rba_merge, the last merge writing the bf16 output) followed by the
-backward ring replay (rba_bwd_preprocess, then 8 rba_bwd_step launches).
+backward ring replay (rba_bwd_preprocess on the merged fp32 output, then 8
+rba_bwd_step launches).
 Workload: causal zigzag split of a 32768-token sequence over 8 virtual
 ranks, rank 3 (pieces 3 and 12, 4096 queries), 32 query / 8 KV heads,
 d = 128, bf16, inputs N(0,1) plus a seeded dO.
@@ -156,8 +157,8 @@ def main():
         elif kind == "merge":
             # 12d+12 bytes per (row, head); the last merge of each replay also writes bf16 O
             work = len(items) * (12 * d + 12) * sq * hq + args.steps * 2 * d * sq * hq
-        else:   # preprocess: reads O and dO (bf16), writes delta
-            work = len(items) * (4 * d + 4) * sq * hq
+        else:   # preprocess: reads O (fp32 accumulator) and dO (bf16), writes delta
+            work = len(items) * (6 * d + 4) * sq * hq
         kern[kind] = {"launches": len(items), "total_ms": tot, "avg_us": 1e3 * tot / len(items), "work": work}
     dom = max(("fwd", "bwd"), key=lambda k: kern[k]["total_ms"])
     dk = kern[dom]

@@ -139,10 +139,12 @@ int rba_merge(int64_t sq, int32_t hq, int32_t d,
 
 /*
  * rba_bwd_preprocess — delta[h, i] = sum_c dO[i, h, c] * O[i, h, c], fp32.
- *   o and d_o [sq, hq, d] in `dtype` (the saved forward output and its
- *   upstream gradient); delta [hq, sq] fp32.  Run once per backward pass.
+ *   o [sq, hq, d] in o_dtype (the forward's merged output: the fp32
+ *   accumulator gives delta without the output's bf16 rounding), d_o
+ *   [sq, hq, d] in do_dtype (its upstream gradient); delta [hq, sq] fp32.
+ *   Run once per backward pass.
  */
-int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t dtype,
+int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32_t do_dtype,
                        const void* o, const void* d_o, float* delta, void* stream);
 
 /*

@@ -12,8 +12,8 @@
 //
 // gfx950 design
 //   * A workgroup owns 128 keys of one KV head and one query head of its
-//     group (4 waves x 32 keys).  Each wave keeps its K and V rows in
-//     registers as MFMA B operands, and its dK / dV accumulators in registers
+//     group (4 waves x 32 keys).  Each wave keeps its V rows in registers as
+//     MFMA B operands, and its dK / dV accumulators in registers
 //     for the whole pass over the 32-row query blocks that can see those
 //     keys.  Splitting the group's query heads over workgroups balances the
 //     causal work (low key tiles see every query block); the group's partial
@@ -25,17 +25,21 @@
 //     A operands straight from the accumulator registers.  The matching B
 //     operands (dO and Q with the query index along k) come from the same
 //     row-major LDS tiles through the LDS transpose load, with the k order
-//     permuted to match the accumulator rows.
-//   * dQ = dS K needs the other orientation: dS goes through LDS once, and
-//     each wave computes a 32-column slice of dQ over all 128 keys (K read
-//     from a row-major LDS tile through the transpose load), then adds it to
-//     dq_acc with fp32 atomics (consecutive lanes hit consecutive addresses).
-//   * Software pipeline with one barrier per block: block i is staged into
-//     one half of double-buffered LDS tiles, then (after the barrier) the
-//     dQ of block i - 1 is computed and its atomics issued, the loads of
-//     block i + 1 are issued, and block i is computed.  Loads retire in issue
-//     order, so waiting for block i + 1's data never waits for atomics that
-//     were issued after it.
+//     permuted to match the accumulator rows.  K^T (the B operand of S) is
+//     read from the K tile; V stays in registers.
+//   * dQ = dS K needs the other orientation: dS goes through LDS once,
+//     stored transposed ([key][query], aligned 8-byte writes of 4 queries per
+//     lane) and read back as dQ's A operand with the transpose load; each wave
+//     computes a 32-column slice of dQ over all 128 keys (K read from the K
+//     tile through the transpose load), then adds it to dq_acc with fp32
+//     atomics (consecutive lanes hit consecutive addresses).
+//   * The K tile, and each query block's Q, dO, LSE and delta rows, stream
+//     from HBM straight into LDS (global_load_lds; Q / dO double-buffered,
+//     rows unpadded with an XOR chunk swizzle).  Iteration i: wait for block
+//     i's loads and barrier; dQ of block i - 1 (atomics); issue block i + 1's
+//     loads; compute block i; barrier; write block i's dS.  Loads and atomics
+//     may retire out of order, so the wait is a full one, but everything it
+//     covers was issued a whole block of compute earlier.
 #include "rba_device.h"
 
 namespace rba {
@@ -103,18 +107,17 @@ __device__ __forceinline__ int classify_keys(int mask, PosRange k, bool k_bad, i
 
 template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
-  constexpr int TS = D + 16;       // row stride of the Q, dO and K tiles
-  constexpr int SST = kBK + 8;     // dS tile (per query row)
-  constexpr int NCH = (kBQ * D / 8 + kBwdThreads - 1) / kBwdThreads;   // 16-byte chunks per thread
-  // Q, dO and dS tiles are double-buffered: block i is staged and computed in
-  // buffer i % 2 while the dQ of block i - 1 still reads dS buffer (i-1) % 2.
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][kBQ * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][kBQ * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBK * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][kBQ * SST];
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][kBQ];
-  __shared__ __attribute__((aligned(16))) float dlt_lds[2][kBQ];
-  __shared__ int32_t qpos_lds[2][kBQ];
+  constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
+  constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
+  constexpr int QT = kBQ * RB;               // bytes of a Q or dO block tile
+  constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
+  constexpr int SST = kBQ + 4;               // dS^T tile row stride (elements): 72 bytes
+  // K tile (once), double-buffered Q / dO tiles and LSE / delta rows (loaded
+  // straight from HBM into LDS), and the dS tile of the current block.
+  __shared__ __attribute__((aligned(16))) char k_lds[kBK * RB];
+  __shared__ __attribute__((aligned(16))) char qd_lds[2][2][QT];          // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kBQ];       // [buffer][lse | delta]
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kBK * SST];       // dS^T [key][query]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -129,6 +132,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
   const uint16_t* dobase = static_cast<const uint16_t*>(p.d_o);
 
+  // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
+#pragma unroll
+  for (int i = 0; i < kBK / ROWS_PER_LOAD / 4; ++i) {
+    const int ld = wave * (kBK / ROWS_PER_LOAD / 4) + i;
+    const int r = ld * ROWS_PER_LOAD + lane / CPR;
+    const int c = (lane % CPR) ^ tile_swz<CPR>(r);
+    const int krow = min(kr0 + r, p.sk - 1);
+    load_lds16(kbase + ((size_t)krow * p.hkv + g) * D + c * 8, k_lds + ld * 1024);
+  }
+
   // This wave's 32 keys: rows kr0 + 32*wave + col.
   const int wk0 = kr0 + 32 * wave;
   const int wk1 = min(wk0 + 32, p.sk);
@@ -137,18 +150,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   if (wave_any) wkr = pos_range(p.ks, wk0, wk1);
   const bool wave_ragged = wk1 - wk0 < 32;
 
-  // K and V rows as B operands (lane: key col, d = 16*ks + 8*half + 0..7).
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // V rows as B operands of dP = dO V^T (lane: key col, d = 16*ks + 8*half + 0..7).
+  bf16x8 vreg[D / 16];
   {
-    const int krow = wk0 + col;
-    const bool ok = krow < p.sk;
-    const size_t off = ((size_t)(ok ? krow : 0) * p.hkv + g) * D;
+    const int krow = min(wk0 + col, p.sk - 1);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(vbase + ((size_t)krow * p.hkv + g) * D);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 z = {};
-      kreg[ks] = ok ? reinterpret_cast<const bf16x8*>(kbase + off)[2 * ks + half] : z;
-      vreg[ks] = ok ? reinterpret_cast<const bf16x8*>(vbase + off)[2 * ks + half] : z;
-    }
+    for (int ks = 0; ks < D / 16; ++ks) vreg[ks] = src[2 * ks + half];
   }
   const int my_krow = wk0 + col;
   const int32_t my_kpos = my_krow < p.sk ? row_to_pos(p.ks, my_krow) : INT32_MAX;
@@ -162,15 +170,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     }
   }
 
-  // Row-major K tile of the workgroup (dQ's B operand, via the transpose load).
-  for (int c = tid; c < kBK * D / 8; c += kBwdThreads) {
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    const int krow = kr0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (krow < p.sk) val = *reinterpret_cast<const u32x4*>(kbase + ((size_t)krow * p.hkv + g) * D + c8 * 8);
-    *reinterpret_cast<u32x4*>(&k_lds[r * TS + c8 * 8]) = val;
-  }
-
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
@@ -181,138 +180,126 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   if (p.mask != kMaskNone) q_lo = tkr.lo;
   if (p.mask == kMaskDoc) q_hi = (int64_t)doc_end(p.cu, p.n_docs, tkr.hi) - 1;
 
-  // Prefetch registers for one query block.  Nothing reads them before the
-  // block is staged one iteration later, so the loads stay in flight during
-  // a whole block of compute.
-  u32x4 pq[NCH], pdo[NCH];
-  float plse = 0.f, pdlt = 0.f;
-  auto fetch = [&](const QIter& b) {
+  // Direct-to-LDS loads of query block b into buffer `buf`: Q and dO rows
+  // (rows past the end re-read the last row and are masked) and, from wave
+  // 0, the block's LSE (lanes 0-31) and delta (lanes 32-63).
+  auto issue = [&](const QIter& b, int buf) {
     const int qr0 = b.qbk * kBQ;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kBwdThreads * i;
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      const int qrow = qr0 + r;
-      pq[i] = u32x4{0u, 0u, 0u, 0u};
-      pdo[i] = u32x4{0u, 0u, 0u, 0u};
-      if (c < kBQ * D / 8 && qrow < p.sq) {
-        const size_t off = ((size_t)qrow * p.hq + h) * D + c8 * 8;
-        pq[i] = *reinterpret_cast<const u32x4*>(qbase + off);
-        pdo[i] = *reinterpret_cast<const u32x4*>(dobase + off);
-      }
+    for (int i = 0; i < kBQ / ROWS_PER_LOAD / 4; ++i) {
+      const int ld = wave * (kBQ / ROWS_PER_LOAD / 4) + i;
+      const int r = ld * ROWS_PER_LOAD + lane / CPR;
+      const int c = (lane % CPR) ^ tile_swz<CPR>(r);
+      const size_t off = ((size_t)min(qr0 + r, p.sq - 1) * p.hq + h) * D + c * 8;
+      load_lds16(qbase + off, qd_lds[buf][0] + ld * 1024);
+      load_lds16(dobase + off, qd_lds[buf][1] + ld * 1024);
     }
-    if (tid < kBQ && qr0 + tid < p.sq) {
-      plse = p.lse[(size_t)h * p.sq + qr0 + tid];
-      pdlt = p.delta[(size_t)h * p.sq + qr0 + tid];
+    if (wave == 0) {
+      const size_t row = (size_t)h * p.sq + min(qr0 + (lane & 31), p.sq - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(half ? p.delta + row : p.lse + row),
+          (__attribute__((address_space(3))) void*)ld_lds[buf], 4, 0, 0);
     }
   };
 
-  // dQ[:, slice] += scale * dS K over the 128 keys of the tile, for the block
-  // whose dS sits in buffer `buf` (rows qr0..).
-  auto dq_block = [&](int buf, int qr0) {
+  // dQ[:, slice] += scale * dS K over the 128 keys of the tile (rows past the
+  // end add 0 to the last row).
+  auto dq_block = [&](int qr0) {
     constexpr int NDB = D / 32;                    // column slices
     constexpr int KSPLIT = 4 / NDB;                // waves per slice
     constexpr int KEYS = kBK / KSPLIT;
     constexpr int NKS = KEYS / 16;
     const int wd = wave % NDB, kh = wave / NDB;
-    // all operands first, then two independent accumulation chains
-    bf16x8 a[NKS], b[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int key0 = kh * KEYS + 16 * ks + 8 * half;
-      a[ks] = *reinterpret_cast<const bf16x8*>(&ds_lds[buf][col * SST + key0]);
-      b[ks] = tr_operand(k_lds, TS, key0, key0 + 4, wd * 32, lane);
-    }
+    // operands in groups of 4 k-steps (register budget), two accumulation chains
+    constexpr int G4 = NKS < 4 ? NKS : 4;
     f32x16 q0 = {}, q1 = {};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ks += 2) {
-      q0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], q0, 0, 0, 0);
-      q1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks + 1], b[ks + 1], q1, 0, 0, 0);
+    for (int k0 = 0; k0 < NKS; k0 += G4) {
+      bf16x8 a[G4], b[G4];
+#pragma unroll
+      for (int i = 0; i < G4; ++i) {
+        const int key0 = kh * KEYS + 16 * (k0 + i) + 8 * half;
+        a[i] = tr_operand(ds_lds, SST, key0, key0 + 4, 0, lane);     // dS rows = queries
+        b[i] = tr_operand_swz<CPR>(k_lds, key0, key0 + 4, wd * 32, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < G4; i += 2) {
+        q0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], q0, 0, 0, 0);
+        q1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i + 1], b[i + 1], q1, 0, 0, 0);
+      }
     }
-    // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col.
-    // 32-bit element offsets from the uniform base (dq_acc is below 2^32
-    // bytes, checked on the host); the row offsets are scalar multiples.
+    // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col.  32-bit
+    // element offsets from the uniform base (dq_acc < 2^32 bytes, checked on
+    // the host).
     const uint32_t row_stride = (uint32_t)p.hq * D;
-    float* base = p.dq + (((uint32_t)(qr0 + 4 * half) * p.hq + h) * D + wd * 32 + col);
-    if (qr0 + kBQ <= p.sq) {
+    float* base = p.dq + ((uint32_t)h * D + wd * 32 + col);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t r = 8 * (j >> 2) + (j & 3);
-        unsafeAtomicAdd(base + r * row_stride, (q0[j] + q1[j]) * p.scale);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t r = 8 * (j >> 2) + (j & 3);
-        if (qr0 + 4 * half + (int)r < p.sq) unsafeAtomicAdd(base + r * row_stride, (q0[j] + q1[j]) * p.scale);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int qrow = qr0 + 4 * half + 8 * (j >> 2) + (j & 3);
+      const bool ok = qrow < p.sq;
+      unsafeAtomicAdd(base + (uint32_t)(ok ? qrow : p.sq - 1) * row_stride, ok ? (q0[j] + q1[j]) * p.scale : 0.f);
     }
   };
 
   QIter it{-1, 0, 0, 0, true};
   qiter_next(it, p, q_lo, q_hi);
-  if (it.valid) fetch(it);
+  if (it.valid) issue(it, 0);
   int buf = 0;
-  int prev_qr0 = -1;      // block whose dQ is pending
+  int prev_qr0 = -1;      // block whose dS waits in ds_lds for its dQ
 
   while (it.valid) {
     const int qr0 = it.qbk * kBQ;
     const int qr1 = min(qr0 + kBQ, p.sq);
-    // Stage block i into buffer `buf`.  Its previous readers (block i - 2)
-    // finished before the last barrier.
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kBwdThreads * i;
-      if (c < kBQ * D / 8) {
-        const int r = c / (D / 8), c8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(&q_lds[buf][r * TS + c8 * 8]) = pq[i];
-        *reinterpret_cast<u32x4*>(&do_lds[buf][r * TS + c8 * 8]) = pdo[i];
-      }
-    }
-    const PosRange qr = pos_range(p.qs, qr0, qr1);
-    if (tid < kBQ) {
-      const int qrow = qr0 + tid;
-      const bool ok = qrow < p.sq;
-      // log2-domain LSE; rows past the end get +inf so that P = 0
-      lse_lds[buf][tid] = ok ? plse * 1.4426950408889634f : INFINITY;
-      dlt_lds[buf][tid] = ok ? pdlt : 0.f;
-      qpos_lds[buf][tid] = !ok ? kPosNone : (qr.single ? qr.lo + tid : row_to_pos(p.qs, qrow));
-    }
+    // This block's loads have landed (the wait also covers the previous
+    // block's dQ atomics, issued a whole block of compute ago); after the
+    // barrier every wave's loads are visible and the other buffers are free.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // dQ of the previous block (its dS is complete in the other buffer),
-    // then the next block's loads: both stay in flight while this block runs.
-    if (prev_qr0 >= 0) dq_block(buf ^ 1, prev_qr0);
+    // dQ of the previous block, then the next block's loads: both stay in
+    // flight while this block is computed.
+    if (prev_qr0 >= 0) dq_block(prev_qr0);
     QIter nx = it;
     qiter_next(nx, p, q_lo, q_hi);
-    if (nx.valid) fetch(nx);
+    if (nx.valid) issue(nx, buf ^ 1);
 
-    // Class of this wave's keys against the block's queries.
-    const int cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
-    const uint16_t* qt = q_lds[buf];
-    const uint16_t* dot = do_lds[buf];
+    const PosRange qr = pos_range(p.qs, qr0, qr1);
+    int cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
+    const bool q_ragged = qr1 - qr0 < kBQ;
+    if (cls == kFull && q_ragged) cls = kPartial;
+    const char* qt = qd_lds[buf][0];
+    const char* dot = qd_lds[buf][1];
 
     f32x16 sacc = {}, dpacc = {};
     if (cls != kSkip) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qt[col * TS + 16 * ks + 8 * half]);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dot[col * TS + 16 * ks + 8 * half]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], sacc, 0, 0, 0);
+        const int cq = ((2 * ks + half) ^ tile_swz<CPR>(col)) << 4;
+        const int kr = 32 * wave + col;
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + col * RB + cq);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dot + col * RB + cq);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(k_lds + kr * RB + (((2 * ks + half) ^ tile_swz<CPR>(kr)) << 4));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dpacc, 0, 0, 0);
       }
       // P and dS in place (rows: queries 8*(j/4) + 4*half + j%4; column: my key).
+      const float* lse_b = ld_lds[buf];
+      const float* dlt_b = ld_lds[buf] + kBQ;
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int qb0 = 8 * j4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[buf][qb0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_lds[buf][qb0]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_b[qb0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_b[qb0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * j4 + i;
-          float pv = fast_exp2(fmaf(sacc[j], p.scale_log2, -l4[i]));
+          float pv = fast_exp2(fmaf(sacc[j], p.scale_log2, -l4[i] * 1.4426950408889634f));
           if (cls == kPartial) {
-            const int32_t qp = qpos_lds[buf][qb0 + i];
-            const bool ok = my_krow < p.sk && (p.mask == kMaskNone || (my_kpos <= qp && qp < my_kend));
+            const int qrow = qr0 + qb0 + i;
+            bool ok = my_krow < p.sk && qrow < p.sq;
+            if (p.mask != kMaskNone) {
+              const int32_t qp = qr.single ? qr.lo + (qrow - qr0) : row_to_pos(p.qs, min(qrow, p.sq - 1));
+              ok = ok && my_kpos <= qp && qp < my_kend;
+            }
             pv = ok ? pv : 0.f;
           }
           sacc[j] = pv;
@@ -333,19 +320,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
         const int rA = 16 * t2 + 4 * half, rB = rA + 8;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 bdo = tr_operand(dot, TS, rA, rB, db * 32, lane);
-          const bf16x8 bq = tr_operand(qt, TS, rA, rB, db * 32, lane);
+          const bf16x8 bdo = tr_operand_swz<CPR>(dot, rA, rB, db * 32, lane);
+          const bf16x8 bq = tr_operand_swz<CPR>(qt, rA, rB, db * 32, lane);
           dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bdo, dvacc[db], 0, 0, 0);
           dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, bq, dkacc[db], 0, 0, 0);
         }
       }
     }
-    // dS (bf16) to LDS as ds_lds[buf][query][key]; skipped waves write zeros.
+    // Every wave is past the previous block's dQ: dS (bf16) of this block
+    // replaces it, transposed as ds_lds[key][query] so that each lane's four
+    // consecutive queries are one aligned 8-byte write; skipped waves write
+    // zeros.
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qq = 8 * (j >> 2) + 4 * half + (j & 3);
-      const __bf16 v = (__bf16)(cls != kSkip ? dpacc[j] : 0.f);
-      ds_lds[buf][qq * SST + 32 * wave + col] = __builtin_bit_cast(uint16_t, v);
+    for (int j4 = 0; j4 < 4; ++j4) {
+      u32x2 w = {0u, 0u};
+      if (cls != kSkip) {
+        w[0] = pack_bf16x2(dpacc[4 * j4], dpacc[4 * j4 + 1]);
+        w[1] = pack_bf16x2(dpacc[4 * j4 + 2], dpacc[4 * j4 + 3]);
+      }
+      *reinterpret_cast<u32x2*>(&ds_lds[(32 * wave + col) * SST + 8 * j4 + 4 * half]) = w;
     }
     prev_qr0 = qr0;
     buf ^= 1;
@@ -353,7 +347,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   }
   if (prev_qr0 >= 0) {
     __syncthreads();
-    dq_block(buf ^ 1, prev_qr0);
+    dq_block(prev_qr0);
   }
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).

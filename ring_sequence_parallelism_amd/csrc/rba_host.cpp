@@ -318,20 +318,23 @@ int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, c
   return hip_status(rba::launch_merge(p, (hipStream_t)stream), "merge");
 }
 
-int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t dtype, const void* o, const void* d_o,
-                       float* delta, void* stream) {
+int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32_t do_dtype, const void* o,
+                       const void* d_o, float* delta, void* stream) {
   g_err.clear();
   int rc;
   if ((rc = check_rows(sq, "preprocess"))) return rc;
   if (hq < 1) return fail(RBA_ERR_INVALID, "hq = %d", hq);
   if (d != 64 && d != 128) return fail(RBA_ERR_UNSUPPORTED, "head dimension %d (supported: 64, 128)", d);
-  if (dtype != RBA_BF16 && dtype != RBA_F32) return fail(RBA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (o_dtype != RBA_BF16 && o_dtype != RBA_F32) return fail(RBA_ERR_INVALID, "unknown O dtype %d", o_dtype);
+  if (do_dtype != RBA_BF16 && do_dtype != RBA_F32) return fail(RBA_ERR_INVALID, "unknown dO dtype %d", do_dtype);
   if ((rc = check_ptr(o, "o")) || (rc = check_ptr(d_o, "d_o")) || (rc = check_ptr(delta, "delta"))) return rc;
   if (sq == 0) return RBA_OK;
   if ((rc = check_device())) return rc;
   rba::PrepParams p{};
   p.o = o; p.d_o = d_o; p.delta = delta;
-  p.n_pairs = sq * hq; p.sq = (int32_t)sq; p.hq = hq; p.d = d; p.bf16 = dtype == RBA_BF16;
+  p.n_pairs = sq * hq; p.sq = (int32_t)sq; p.hq = hq; p.d = d;
+  p.o_bf16 = o_dtype == RBA_BF16;
+  p.do_bf16 = do_dtype == RBA_BF16;
   return hip_status(rba::launch_bwd_preprocess(p, (hipStream_t)stream), "backward preprocess");
 }
 

@@ -79,7 +79,7 @@ struct PrepParams {
   float* delta;
   int64_t n_pairs;
   int32_t sq, hq, d;
-  int32_t bf16;
+  int32_t o_bf16, do_bf16;   // element types of O and dO (1: bf16, 0: fp32)
 };
 
 // Launchers (defined next to their kernels).  Each returns the launch status.

@@ -56,30 +56,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   }
 }
 
-// delta[h, i] = sum_c dO[i, h, c] * O[i, h, c]
+// delta[h, i] = sum_c dO[i, h, c] * O[i, h, c].  Each thread takes 4
+// consecutive elements of one (row, head) pair from both tensors (8 or 16
+// bytes per load, by element type).
+__device__ __forceinline__ f32x4 load4(const void* base, size_t i, bool bf16) {
+  if (bf16) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  }
+  return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+}
+
 __global__ __launch_bounds__(kMergeThreads) void bwd_preprocess_kernel(PrepParams p) {
-  const int per = p.bf16 ? 8 : 4;                 // elements per 16-byte vector
-  const int tpp = p.d / per;                      // threads per pair (power of two, <= 16)
+  const int tpp = p.d / 4;                        // threads per pair (power of two, <= 32)
   const int ppb = kMergeThreads / tpp;
   const int sub = threadIdx.x / tpp, c = threadIdx.x % tpp;
   for (int64_t base = (int64_t)blockIdx.x * ppb; base < p.n_pairs; base += (int64_t)gridDim.x * ppb) {
     const int64_t pair = base + sub;
     float acc = 0.f;
     if (pair < p.n_pairs) {
-      const size_t oi = (size_t)pair * p.d + (size_t)c * per;
-      if (p.bf16) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + oi);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.d_o) + oi);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
-          acc += __uint_as_float(a[i] & 0xffff0000u) * __uint_as_float(b[i] & 0xffff0000u);
-        }
-      } else {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + oi);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.d_o) + oi);
-        acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-      }
+      const size_t i = (size_t)pair * p.d + (size_t)c * 4;
+      const f32x4 a = load4(p.o, i, p.o_bf16), b = load4(p.d_o, i, p.do_bf16);
+      acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
     }
     // reduce over the tpp consecutive lanes of the pair
     for (int off = tpp >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -103,8 +102,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s) {
-  const int per = p.bf16 ? 8 : 4;
-  const int ppb = kMergeThreads / (p.d / per);
+  const int ppb = kMergeThreads / (p.d / 4);
   hipLaunchKernelGGL(bwd_preprocess_kernel, dim3(grid_for(p.n_pairs, ppb)), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }

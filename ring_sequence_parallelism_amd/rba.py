@@ -89,7 +89,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     A, S = ctypes.POINTER(rba_attn), ctypes.POINTER(rba_segs)
     lib.rba_fwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P]
     lib.rba_merge.argtypes = [I64, I32, I32, P, P, P, P, P, I32, P]
-    lib.rba_bwd_preprocess.argtypes = [I64, I32, I32, I32, P, P, P, P]
+    lib.rba_bwd_preprocess.argtypes = [I64, I32, I32, I32, I32, P, P, P, P]
     lib.rba_bwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
     for fn in ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_plan_step"):
@@ -120,10 +120,11 @@ def _check(fn: str, rc: int) -> int:
 
 def attn_params(hq: int, hkv: int, d: int, scale: float, dtype: int, mask: int,
                 cu_seqlens_dev: Optional[torch.Tensor] = None, cu_seqlens_host=None) -> rba_attn:
-    """Build an rba_attn.  cu_seqlens_host (a numpy int32 array) is kept alive on the struct."""
+    """Build an rba_attn.  Both cu_seqlens arrays are kept alive on the struct."""
     a = rba_attn()
     a.hq, a.hkv, a.d, a.scale, a.dtype, a.mask = hq, hkv, d, scale, dtype, mask
     a.cu_seqlens_dev = None if cu_seqlens_dev is None else cu_seqlens_dev.data_ptr()
+    a._cu_dev_keepalive = cu_seqlens_dev   # the struct holds a raw pointer into it
     a.n_docs = 0
     if cu_seqlens_host is not None:
         import numpy as np
@@ -151,10 +152,18 @@ def rba_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None, final_dt
         final_dtype, _stream(stream)))
 
 
-def rba_bwd_preprocess(o, d_o, delta, dtype: int = RBA_BF16, stream=None) -> int:
+def _dtype_of(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return RBA_BF16
+    if t.dtype == torch.float32:
+        return RBA_F32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def rba_bwd_preprocess(o, d_o, delta, stream=None) -> int:
     sq, hq, d = o.shape
     return _check("rba_bwd_preprocess", load().rba_bwd_preprocess(
-        sq, hq, d, dtype, _ptr(o), _ptr(d_o), _ptr(delta), _stream(stream)))
+        sq, hq, d, _dtype_of(o), _dtype_of(d_o), _ptr(o), _ptr(d_o), _ptr(delta), _stream(stream)))
 
 
 def rba_bwd_step(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, d_o, lse, delta,

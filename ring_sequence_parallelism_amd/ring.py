@@ -147,15 +147,15 @@ class RingReplay:
                  stream=None, on_step=None):
         """dq (fp32, accumulated over steps) and per-step dk / dv by source rank.
 
-        Uses the forward's saved output (``o_final`` by default) and merged LSE.
-        Steps the host proves empty leave their dk / dv zero.
+        Uses the forward's merged output (the fp32 accumulator by default) and
+        merged LSE.  Steps the host proves empty leave their dk / dv zero.
         """
         assert self.with_grad
-        o_saved = self.o_final if o_saved is None else o_saved
+        o_saved = self.o_acc if o_saved is None else o_saved
         lse_saved = self.lse_acc if lse_saved is None else lse_saved
         if on_step:
             on_step("prep", -1)
-        rba.rba_bwd_preprocess(o_saved, self.d_o, self.delta, self.dtype, stream)
+        rba.rba_bwd_preprocess(o_saved, self.d_o, self.delta, stream)
         self.dq.zero_()
         for i, s in enumerate(self.steps):
             if s.status != rba.RBA_OK:

@@ -112,7 +112,8 @@ def test_merge_and_preprocess_validation():
     assert lib.rba_merge(8, 2, 64, FAKE, FAKE, FAKE, None, None, 0, None) == rba.RBA_ERR_INVALID
     assert lib.rba_merge(8, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == rba.RBA_ERR_INVALID  # alias
     assert lib.rba_merge(8, 2, 64, FAKE, FAKE, None, None, None, 0, None) == rba.RBA_OK          # nothing to do
-    assert lib.rba_bwd_preprocess(8, 2, 96, 0, FAKE, FAKE, FAKE, None) == rba.RBA_ERR_UNSUPPORTED
+    assert lib.rba_bwd_preprocess(8, 2, 96, 0, 0, FAKE, FAKE, FAKE, None) == rba.RBA_ERR_UNSUPPORTED
+    assert lib.rba_bwd_preprocess(8, 2, 64, 0, 5, FAKE, FAKE, FAKE, None) == rba.RBA_ERR_INVALID
 
 
 def test_bwd_rejects_f32():

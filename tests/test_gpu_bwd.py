@@ -38,6 +38,12 @@ def test_preprocess():
         torch.cuda.synchronize()
         want = (o64 * d64).sum(axis=2).T
         np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-4)
+        # fp32 output (the merged accumulator) with a bf16 gradient
+        of = rng.standard_normal((333, 6, d)).astype(np.float32)
+        rba.rba_bwd_preprocess(torch.from_numpy(of).to(DEV), to_device(db, "bf16", DEV), delta)
+        torch.cuda.synchronize()
+        want = (of.astype(np.float64) * d64).sum(axis=2).T
+        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-4)
 
 
 def _pos(segs):
@@ -83,7 +89,7 @@ def test_step_single_chunk(case):
     assert rba.rba_fwd_step(a, q, qs, k, v, ks, o_acc, lse) == rba.RBA_OK
     rba.rba_merge(o_acc, lse, None, None, o_fin, rba.RBA_BF16)
     delta = torch.empty((hq, sq), device=DEV)
-    rba.rba_bwd_preprocess(o_fin, dO, delta)
+    rba.rba_bwd_preprocess(o_acc, dO, delta)
     dq = torch.zeros((sq, hq, d), device=DEV)
     dk = torch.full((sk, hkv, d), float("nan"), device=DEV)
     dv = torch.full((sk, hkv, d), float("nan"), device=DEV)
