@@ -119,7 +119,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kBQ];       // [buffer][lse | delta]
   __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kBK * SST];       // dS^T [key][query]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int col = lane & 31, half = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, p.n_wg);
   const int g = logical / (p.n_key_tiles * p.group);
@@ -127,10 +128,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   const int h = g * p.group + logical % p.group;   // the query head of this workgroup
   const int kr0 = kt * kBK;
   const int kr1 = min(kr0 + kBK, p.sk);
-  const uint16_t* qbase = static_cast<const uint16_t*>(p.q);
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
-  const uint16_t* dobase = static_cast<const uint16_t*>(p.d_o);
+  // Uniform bases of this workgroup's heads and 32-bit row strides in bytes
+  // (q, dO and k are each smaller than 4 GiB, checked on the host).
+  const uint32_t q_row_bytes = (uint32_t)p.hq * RB, k_row_bytes = (uint32_t)p.hkv * RB;
+  const char* qg = static_cast<const char*>(p.q) + (size_t)h * RB;
+  const char* dog = static_cast<const char*>(p.d_o) + (size_t)h * RB;
+  const char* kg = static_cast<const char*>(p.k) + (size_t)g * RB;
 
   // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
 #pragma unroll
@@ -138,8 +142,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     const int ld = wave * (kBK / ROWS_PER_LOAD / 4) + i;
     const int r = ld * ROWS_PER_LOAD + lane / CPR;
     const int c = (lane % CPR) ^ tile_swz<CPR>(r);
-    const int krow = min(kr0 + r, p.sk - 1);
-    load_lds16(kbase + ((size_t)krow * p.hkv + g) * D + c * 8, k_lds + ld * 1024);
+    const uint32_t krow = (uint32_t)min(kr0 + r, p.sk - 1);
+    dma16(kg, krow * k_row_bytes + (uint32_t)(c << 4), lds_addr(k_lds) + ld * 1024);
   }
 
   // This wave's 32 keys: rows kr0 + 32*wave + col.
@@ -182,23 +186,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
 
   // Direct-to-LDS loads of query block b into buffer `buf`: Q and dO rows
   // (rows past the end re-read the last row and are masked) and, from wave
-  // 0, the block's LSE (lanes 0-31) and delta (lanes 32-63).
+  // 0, the block's LSE (lanes 0-31) and delta (lanes 32-63).  The per-lane
+  // byte offsets inside a full block are loop invariant.
+  constexpr int QLOADS = kBQ / ROWS_PER_LOAD / 4;
+  uint32_t qoff[QLOADS];
+#pragma unroll
+  for (int i = 0; i < QLOADS; ++i) {
+    const int r = (wave * QLOADS + i) * ROWS_PER_LOAD + lane / CPR;
+    qoff[i] = (uint32_t)r * q_row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
+  }
+  const uint32_t qd_wave = lds_addr(&qd_lds[0][0][0]) + wave * QLOADS * 1024;
+  const uintptr_t lse_row = (uintptr_t)(p.lse + (size_t)h * p.sq);
+  const uintptr_t dlt_row = (uintptr_t)(p.delta + (size_t)h * p.sq);
+  const uintptr_t ld_src = half ? dlt_row : lse_row;    // per lane, from two uniform values
   auto issue = [&](const QIter& b, int buf) {
     const int qr0 = b.qbk * kBQ;
+    const uint32_t dst = qd_wave + buf * 2 * QT;
+    if (qr0 + kBQ <= p.sq) {
+      const size_t bb = (size_t)qr0 * q_row_bytes;
 #pragma unroll
-    for (int i = 0; i < kBQ / ROWS_PER_LOAD / 4; ++i) {
-      const int ld = wave * (kBQ / ROWS_PER_LOAD / 4) + i;
-      const int r = ld * ROWS_PER_LOAD + lane / CPR;
-      const int c = (lane % CPR) ^ tile_swz<CPR>(r);
-      const size_t off = ((size_t)min(qr0 + r, p.sq - 1) * p.hq + h) * D + c * 8;
-      load_lds16(qbase + off, qd_lds[buf][0] + ld * 1024);
-      load_lds16(dobase + off, qd_lds[buf][1] + ld * 1024);
+      for (int i = 0; i < QLOADS; ++i) {
+        dma16(qg + bb, qoff[i], dst + i * 1024);
+        dma16(dog + bb, qoff[i], dst + QT + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QLOADS; ++i) {
+        const int r = (wave * QLOADS + i) * ROWS_PER_LOAD + lane / CPR;
+        const uint32_t off = (uint32_t)min(qr0 + r, p.sq - 1) * q_row_bytes +
+                             (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
+        dma16(qg, off, dst + i * 1024);
+        dma16(dog, off, dst + QT + i * 1024);
+      }
     }
     if (wave == 0) {
-      const size_t row = (size_t)h * p.sq + min(qr0 + (lane & 31), p.sq - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(half ? p.delta + row : p.lse + row),
-          (__attribute__((address_space(3))) void*)ld_lds[buf], 4, 0, 0);
+      const uintptr_t src = ld_src + 4 * (uintptr_t)min(qr0 + (lane & 31), p.sq - 1);
+      dma4(reinterpret_cast<const void*>(src), lds_addr(ld_lds[buf]));
     }
   };
 

@@ -166,17 +166,66 @@ __device__ __forceinline__ bf16x8 tr_operand_swz(const char* base, int rowA, int
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's data lands
-// at lds_wave_base + 16 * l (lds_wave_base must be the same for the wave).
-__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gptr,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// Round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a): one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+// Direct-to-LDS load, 16 bytes per lane, in the scalar-base form: lane l
+// reads global address sbase + voff (voff a 32-bit byte offset) and its data
+// lands at LDS byte address lds + 16 * l.  sbase and lds must be uniform
+// over the wave.
+//
+// Written as inline assembly so that the compiler does not see an LDS write:
+// it would otherwise make every later LDS read wait for all outstanding
+// direct loads (it cannot tell the double buffers apart), which stalls each
+// tile on the prefetch of the next.  The caller orders these loads against
+// LDS reads itself: s_waitcnt vmcnt(0) and a workgroup barrier before a
+// buffer is read, and a barrier before a buffer that was read is refilled.
+// M0 carries the LDS address; it is saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
+  // The values are uniform by contract; readfirstlane moves them to SGPRs
+  // when the compiler kept a copy in VGPRs (free when already scalar).
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase_in);
+  const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// Direct-to-LDS load of 4 bytes per lane from a per-lane 64-bit address;
+// lane l's dword lands at LDS byte address lds + 4 * l (lds uniform).  Same
+// ordering contract as dma16.
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_in) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds)
+      : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 }  // namespace rba

@@ -37,11 +37,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;  // keys per tile
 
-// Storage slot of key kk (0..63) inside a transposed V tile row.
-__device__ __forceinline__ int vt_slot(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
 // Setup shared by both element types: which rows/head this wave owns and the
 // allowed key interval of the workgroup.
 struct WaveTask {
@@ -54,8 +49,7 @@ struct WaveTask {
 };
 
 template <int QR>
-__device__ __forceinline__ WaveTask make_task(const FwdParams& p) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave) {
   const int logical = xcd_remap(blockIdx.x, p.n_wg);
   const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
   const int rg = logical % p.n_row_groups;
@@ -150,11 +144,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // while tile t + 1 streams into the other one.
   __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<QR>(p);
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
+  const WaveTask t = make_task<QR>(p, wave);
+  const uint32_t row_bytes = (uint32_t)p.hkv * RB;     // stride of a K/V row in global memory
+  const char* kg = static_cast<const char*>(p.k) + (size_t)t.g * RB;
+  const char* vg = static_cast<const char*>(p.v) + (size_t)t.g * RB;
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -174,21 +170,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     qds[qb] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
   }
 
-  // Issue the direct-to-LDS loads of key tile kt into buffer b.  Lane l of
-  // load i writes chunk position l % CPR of tile row (first row + l / CPR);
-  // it fetches the global chunk that the swizzle stores there.  Rows past the
-  // end of the chunk re-read the last row (finite values; masked out).
-  auto issue = [&](int kt, int b) {
+  // Direct-to-LDS loads of key tile kt into buffer b.  Load i of this wave
+  // fills tile rows (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR: lane l
+  // writes chunk position l % CPR of its row and fetches the global chunk that
+  // the swizzle stores there.  The per-lane byte offsets inside a tile are
+  // loop invariant; a whole tile adds a uniform base.  The last, ragged tile
+  // clamps rows past the end of the chunk to its last row (finite values,
+  // masked out).
+  uint32_t loff[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
-      const int cp = lane % CPR;
-      const int c = cp ^ tile_swz<CPR>(r);
-      const int krow = min(kt * kBN + r, p.sk - 1);
-      const size_t off = ((size_t)krow * p.hkv + t.g) * D + c * 8;
-      char* dst = &lds[b][0][(wave * LOADS + i) * 64 * 16];
-      load_lds16(kbase + off, dst);
-      load_lds16(vbase + off, dst + TILE);
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
+    loff[i] = (uint32_t)r * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
+  }
+  const uint32_t lds_wave = lds_addr(&lds[0][0][0]) + wave * LOADS * 1024;
+  auto issue = [&](int kt, int b) {
+    const uint32_t dst = lds_wave + b * 2 * TILE;
+    if ((kt + 1) * kBN <= p.sk) {
+      const size_t tb = (size_t)kt * kBN * row_bytes;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        dma16(kg + tb, loff[i], dst + i * 1024);
+        dma16(vg + tb, loff[i], dst + TILE + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
+        const uint32_t krow = (uint32_t)min(kt * kBN + r, p.sk - 1);
+        const uint32_t off = krow * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
+        dma16(kg, off, dst + i * 1024);
+        dma16(vg, off, dst + TILE + i * 1024);
+      }
     }
   };
 
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<QR>(p);
+  const WaveTask t = make_task<QR>(p, __builtin_amdgcn_readfirstlane(tid >> 6));
   const float* kbase = static_cast<const float*>(p.k);
   const float* vbase = static_cast<const float*>(p.v);
 

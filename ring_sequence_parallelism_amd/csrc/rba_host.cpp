@@ -266,10 +266,12 @@ int rba_fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(o_part, "o_part")) || (rc = check_ptr(lse_part, "lse_part")))
     return rc;
+  const bool bf16 = a->dtype == RBA_BF16;
+  if (bf16 && sk * a->hkv * a->d * 2 >= ((int64_t)1 << 32))
+    return fail(RBA_ERR_UNSUPPORTED, "forward step: k and v must each be smaller than 4 GiB");
   if (plan.empty) return RBA_STEP_EMPTY;
   if ((rc = check_device())) return rc;
 
-  const bool bf16 = a->dtype == RBA_BF16;
   rba::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o_part; p.lse = lse_part;
   p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
@@ -352,6 +354,8 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
     return rc;
   if ((int64_t)sq * a->hq * a->d * 4 >= ((int64_t)1 << 32))
     return fail(RBA_ERR_UNSUPPORTED, "backward step: dq_acc must be smaller than 4 GiB");
+  if (sk * a->hkv * a->d * 2 >= ((int64_t)1 << 32))
+    return fail(RBA_ERR_UNSUPPORTED, "backward step: k and v must each be smaller than 4 GiB");
   if (plan.empty) return RBA_STEP_EMPTY;
   if ((rc = check_device())) return rc;
   rba::BwdParams p{};
