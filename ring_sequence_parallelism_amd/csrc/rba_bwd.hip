@@ -132,9 +132,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   // Uniform bases of this workgroup's heads and 32-bit row strides in bytes
   // (q, dO and k are each smaller than 4 GiB, checked on the host).
   const uint32_t q_row_bytes = (uint32_t)p.hq * RB, k_row_bytes = (uint32_t)p.hkv * RB;
-  const char* qg = static_cast<const char*>(p.q) + (size_t)h * RB;
-  const char* dog = static_cast<const char*>(p.d_o) + (size_t)h * RB;
-  const char* kg = static_cast<const char*>(p.k) + (size_t)g * RB;
+  const char* qg = uniform_ptr(static_cast<const char*>(p.q) + (uint32_t)(h * RB));
+  const char* dog = uniform_ptr(static_cast<const char*>(p.d_o) + (uint32_t)(h * RB));
+  const char* kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(g * RB));
 
   // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
 #pragma unroll

@@ -187,12 +187,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // LDS reads itself: s_waitcnt vmcnt(0) and a workgroup barrier before a
 // buffer is read, and a barrier before a buffer that was read is refilled.
 // M0 carries the LDS address; it is saved and restored around the load.
+// A wave-uniform pointer, pinned to SGPRs (readfirstlane is free when the
+// value already is scalar; 64-bit address arithmetic otherwise tends to stay
+// in VGPRs).
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return reinterpret_cast<const char*>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b));
+}
+
 __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
-  // The values are uniform by contract; readfirstlane moves them to SGPRs
-  // when the compiler kept a copy in VGPRs (free when already scalar).
-  const uint64_t b = reinterpret_cast<uint64_t>(sbase_in);
-  const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  // sbase and lds are uniform by contract; pin them to SGPRs.
+  const char* sbase = uniform_ptr(sbase_in);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
   uint32_t saved;
   asm volatile(

@@ -29,6 +29,8 @@
 //     full (no mask arithmetic) or partial (per-element mask).
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score,
 //     and a lazy running maximum that rarely rescales O.
+#include <type_traits>
+
 #include "rba_device.h"
 
 namespace rba {
@@ -105,7 +107,7 @@ __device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask
 // next tile's loads can be issued before the current tile is computed.
 struct TileIter {
   int s, kt, t1, next_tile;
-  bool valid;
+  int valid;   // int, not bool: a padding-free struct stays in registers
 };
 
 __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, const WaveTask& t) {
@@ -113,7 +115,7 @@ __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, cons
   while (it.kt >= it.t1) {
     ++it.s;
     if (it.s >= p.ks.n) {
-      it.valid = false;
+      it.valid = 0;
       return;
     }
     const int64_t st = p.ks.start[it.s];
@@ -149,8 +151,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int col = lane & 31, half = lane >> 5;
   const WaveTask t = make_task<QR>(p, wave);
   const uint32_t row_bytes = (uint32_t)p.hkv * RB;     // stride of a K/V row in global memory
-  const char* kg = static_cast<const char*>(p.k) + (size_t)t.g * RB;
-  const char* vg = static_cast<const char*>(p.v) + (size_t)t.g * RB;
+  const char* kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(t.g * RB));
+  const char* vg = uniform_ptr(static_cast<const char*>(p.v) + (uint32_t)(t.g * RB));
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -174,34 +176,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // fills tile rows (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR: lane l
   // writes chunk position l % CPR of its row and fetches the global chunk that
   // the swizzle stores there.  The per-lane byte offsets inside a tile are
-  // loop invariant; a whole tile adds a uniform base.  The last, ragged tile
-  // clamps rows past the end of the chunk to its last row (finite values,
-  // masked out).
-  uint32_t loff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
-    loff[i] = (uint32_t)r * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
-  }
+  // loop invariant and a tile adds a uniform base; in the last, ragged tile,
+  // lanes whose row is past the end of the chunk step back to its last row
+  // (finite values, masked out).
+  // Lane offsets: load i covers rows 16 * wave + 4 * i + lane / 16 (d = 128;
+  // 8 * wave + 8 * i + lane / 8 for d = 64), so its row term is a uniform
+  // step of load 0's and its swizzled chunk is load 0's XOR a constant
+  // (tile_swz of the row differs from load 0's by a constant XOR).
+  static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile rows");
+  const int r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;      // row of load 0
+  const uint32_t loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
+  // (swizzle of load i's row) ^ (swizzle of load 0's row), in bytes: rows
+  // 4i apart (d = 128) differ in bit 2 of the row and, from i = 2, bit 3;
+  // rows 8i apart (d = 64) share their swizzle.
+  auto chunk_xor = [](int i) -> uint32_t {
+    return CPR == 16 ? (uint32_t)((8 * (i & 1)) | ((i >> 1) & 1)) << 4 : 0u;
+  };
   const uint32_t lds_wave = lds_addr(&lds[0][0][0]) + wave * LOADS * 1024;
   auto issue = [&](int kt, int b) {
     const uint32_t dst = lds_wave + b * 2 * TILE;
-    if ((kt + 1) * kBN <= p.sk) {
-      const size_t tb = (size_t)kt * kBN * row_bytes;
+    const bool whole = (kt + 1) * kBN <= p.sk;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        dma16(kg + tb, loff[i], dst + i * 1024);
-        dma16(vg + tb, loff[i], dst + TILE + i * 1024);
+    for (int i = 0; i < LOADS; ++i) {
+      size_t tb = ((size_t)kt * kBN + i * ROWS_PER_LOAD) * row_bytes;
+      uint32_t off = loff0 ^ chunk_xor(i);
+      if (!whole) {
+        // Relative to the tile's first row: the clamped row is at or past
+        // it, so the unsigned lane offset never wraps (load i's own first
+        // row may lie past the end of the chunk).
+        tb = (size_t)kt * kBN * row_bytes;
+        off += (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
+        const int over = kt * kBN + r_lane + i * ROWS_PER_LOAD - (p.sk - 1);
+        if (over > 0) off -= (uint32_t)over * row_bytes;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR;
-        const uint32_t krow = (uint32_t)min(kt * kBN + r, p.sk - 1);
-        const uint32_t off = krow * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
-        dma16(kg, off, dst + i * 1024);
-        dma16(vg, off, dst + TILE + i * 1024);
-      }
+      dma16(kg + tb, off, dst + i * 1024);
+      dma16(vg + tb, off, dst + TILE + i * 1024);
     }
   };
 
@@ -215,11 +224,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  TileIter it{-1, 0, 0, 0, true};
+  TileIter it{-1, 0, 0, 0, 1};
   tile_next(it, p, t);
   if (it.valid) issue(it.kt, 0);
-  int buf = 0;
-  while (it.valid) {
+  // The body of one key tile, for a compile-time buffer index (the loop is
+  // unrolled by two so LDS addresses of either buffer are immediate offsets).
+  auto tile = [&](auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int kt = it.kt;
     const int kr0 = kt * kBN;
     const int kr1 = min(kr0 + kBN, p.sk);
@@ -344,8 +355,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    buf ^= 1;
     it = nx;
+  };
+  while (it.valid) {
+    tile(std::integral_constant<int, 0>{});
+    if (!it.valid) break;
+    tile(std::integral_constant<int, 1>{});
   }
 
   // Epilogue: O = O_acc / l, LSE = m ln 2 + ln l; rows with no key: (0, -inf).

@@ -126,6 +126,48 @@ def test_step_fully_masked_rows():
     assert_close(o, wo, "bf16", "o_part")
 
 
+def _run_scaled_keys(sq, sk, hq, hkv, d, mask, qsegs, ksegs, row_scale, seed):
+    rng = np.random.default_rng(seed)
+    qb, q64 = _rand_inputs(rng, sq, hq, d, "bf16")
+    k = rng.standard_normal((sk, hkv, d)).astype(np.float32) * row_scale[:, None, None].astype(np.float32)
+    kb = W.f32_to_bf16_bits(k)
+    k64 = W.bf16_bits_to_f32(kb).astype(np.float64)
+    vb, v64 = _rand_inputs(rng, sk, hkv, d, "bf16")
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    a = rba.attn_params(hq, hkv, d, scale, rba.RBA_BF16, mask)
+    q, kd, v = (to_device(x, "bf16", DEV) for x in (qb, kb, vb))
+    o = torch.full((sq, hq, d), float("nan"), device=DEV)
+    lse = torch.full((hq, sq), float("nan"), device=DEV)
+    st = rba.rba_fwd_step(a, q, rba.make_segs(qsegs), kd, v, rba.make_segs(ksegs), o, lse)
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(q64, k64, v64, _pos(qsegs), _pos(ksegs), mask, scale)
+    return st, o.cpu().numpy(), lse.cpu().numpy(), wo, wl
+
+
+@pytest.mark.parametrize("pattern", ["jump", "ramp", "drop"])
+@pytest.mark.parametrize("mask", [0, 1])
+def test_step_score_range(pattern, mask):
+    # Key norms that change along the chunk move the row maximum by far more
+    # than 2^16 between key tiles (jump, ramp) or leave later tiles far below
+    # it (drop): exercises the running reference, its rescale and the redo of
+    # a tile whose exponentials would leave the accepted range.
+    sq, sk, hq, hkv, d = 96, 448, 4, 2, 128
+    _say("fwd score range", pattern, "mask", mask)
+    rows = np.arange(sk)
+    if pattern == "jump":
+        row_scale = np.where(rows < 64, 0.05, 12.0)
+    elif pattern == "ramp":
+        row_scale = 0.05 + 20.0 * rows / sk
+    else:
+        row_scale = np.where(rows < 128, 12.0, 0.05)
+    # queries after every key: every tile is full under the causal mask too
+    st, o, lse, wo, wl = _run_scaled_keys(sq, sk, hq, hkv, d, mask, [(1000, sq)], [(0, sk)], row_scale,
+                                          11 + mask + 3 * len(pattern))
+    assert st == rba.RBA_OK
+    assert_lse(lse, wl, "lse")
+    assert_close(o, wo, "bf16", "o_part")
+
+
 def test_step_deterministic():
     _say("fwd determinism")
     rng = np.random.default_rng(8)
