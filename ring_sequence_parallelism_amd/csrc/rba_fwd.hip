@@ -179,19 +179,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // loop invariant and a tile adds a uniform base; in the last, ragged tile,
   // lanes whose row is past the end of the chunk step back to its last row
   // (finite values, masked out).
-  // Lane offsets: load i covers rows 16 * wave + 4 * i + lane / 16 (d = 128;
-  // 8 * wave + 8 * i + lane / 8 for d = 64), so its row term is a uniform
-  // step of load 0's and its swizzled chunk is load 0's XOR a constant
-  // (tile_swz of the row differs from load 0's by a constant XOR).
+  // Lane offsets: load i covers rows r_lane + ROWS_PER_LOAD * i, where the
+  // two terms share no set bit (r_lane = 16 * wave + lane / 16 for d = 128,
+  // 16 * wave + lane / 8 for d = 64), so its row term is a uniform step of
+  // load 0's and, tile_swz being XOR-linear, its swizzled chunk is load 0's
+  // XOR tile_swz(ROWS_PER_LOAD * i).
   static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile rows");
   const int r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;      // row of load 0
   const uint32_t loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
-  // (swizzle of load i's row) ^ (swizzle of load 0's row), in bytes: rows
-  // 4i apart (d = 128) differ in bit 2 of the row and, from i = 2, bit 3;
-  // rows 8i apart (d = 64) share their swizzle.
-  auto chunk_xor = [](int i) -> uint32_t {
-    return CPR == 16 ? (uint32_t)((8 * (i & 1)) | ((i >> 1) & 1)) << 4 : 0u;
-  };
+  auto chunk_xor = [](int i) -> uint32_t { return (uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4; };
   const uint32_t lds_wave = lds_addr(&lds[0][0][0]) + wave * LOADS * 1024;
   auto issue = [&](int kt, int b) {
     const uint32_t dst = lds_wave + b * 2 * TILE;
