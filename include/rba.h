@@ -158,10 +158,13 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32
  *   q, d_o [sq, hq, d] (dtype); k, v [sk, hkv, d] (dtype); lse, delta
  *   [hq, sq] fp32; dq_acc [sq, hq, d] fp32; dk_step, dv_step [sk, hkv, d] fp32.
  * On RBA_STEP_EMPTY nothing is launched: dq_acc is unchanged and dk_step /
- * dv_step are NOT written (the step's true dK/dV are zero).  dq_acc is
- * accumulated with fp32 atomics, so its low bits depend on scheduling.
- * dtype RBA_BF16 only, d in {64, 128}; dq_acc must be smaller than 4 GiB
- * (sq * hq * d * 4 bytes), else RBA_ERR_UNSUPPORTED.
+ * dv_step are NOT written (the step's true dK/dV are zero).  Two kernels run
+ * on `stream`: a key-stationary one for dk_step / dv_step (with more than one
+ * query head per KV head, the heads' parts are summed with fp32 atomics into
+ * the zero-filled outputs, so their low bits depend on scheduling) and a
+ * query-stationary one that adds each dq_acc row once (deterministic).
+ * dtype RBA_BF16 only, d in {64, 128}; q, d_o, k and v must each be smaller
+ * than 4 GiB, else RBA_ERR_UNSUPPORTED.
  */
 int rba_bwd_step(const rba_attn* a,
                  const void* q, int64_t sq, const rba_segs* q_segs,

@@ -1,4 +1,5 @@
-// Backward ring step: gradients of L = sum dO * O through one KV chunk.
+// Backward ring step, dK / dV part: gradients of L = sum dO * O with
+// respect to the keys and values of one KV chunk.
 //
 // The pages name training as the workload (HSAP methodology and results;
 // TASP abstract) but print no backward; this is the gradient of the softmax
@@ -7,8 +8,8 @@
 //   dV_j  = sum_i P_ij dO_i
 //   dS_ij = P_ij (<dO_i, v_j> - delta_i)
 //   dK_j  = scale * sum_i dS_ij q_i
-//   dQ_i += scale * sum_j dS_ij k_j
-// summing dK / dV over the query heads that share a KV head (GQA).
+// summing dK / dV over the query heads that share a KV head (GQA).  dQ is
+// computed by the query-stationary kernel in rba_bwd_dq.hip.
 //
 // gfx950 design
 //   * A workgroup owns 128 keys of one KV head and one query head of its
@@ -27,19 +28,12 @@
 //     row-major LDS tiles through the LDS transpose load, with the k order
 //     permuted to match the accumulator rows.  K^T (the B operand of S) is
 //     read from the K tile; V stays in registers.
-//   * dQ = dS K needs the other orientation: dS goes through LDS once,
-//     stored transposed ([key][query], aligned 8-byte writes of 4 queries per
-//     lane) and read back as dQ's A operand with the transpose load; each wave
-//     computes a 32-column slice of dQ over all 128 keys (K read from the K
-//     tile through the transpose load), then adds it to dq_acc with fp32
-//     atomics (consecutive lanes hit consecutive addresses).
 //   * The K tile, and each query block's Q, dO, LSE and delta rows, stream
-//     from HBM straight into LDS (global_load_lds; Q / dO double-buffered,
-//     rows unpadded with an XOR chunk swizzle).  Iteration i: wait for block
-//     i's loads and barrier; dQ of block i - 1 (atomics); issue block i + 1's
-//     loads; compute block i; barrier; write block i's dS.  Loads and atomics
-//     may retire out of order, so the wait is a full one, but everything it
-//     covers was issued a whole block of compute earlier.
+//     from HBM straight into LDS (direct loads; Q / dO double-buffered, rows
+//     unpadded with the XOR chunk swizzle).  Iteration i: wait for block i's
+//     loads and barrier; issue block i + 1's loads; compute block i.
+#include <type_traits>
+
 #include "rba_device.h"
 
 namespace rba {
@@ -63,7 +57,7 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, in
 // workgroup-uniform.
 struct QIter {
   int s, qbk, b1, next_blk;
-  bool valid;
+  int valid;   // int, not bool: a padding-free struct stays in registers
 };
 
 __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_t q_lo, int64_t q_hi) {
@@ -71,7 +65,7 @@ __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_
   while (it.qbk >= it.b1) {
     ++it.s;
     if (it.s >= p.qs.n) {
-      it.valid = false;
+      it.valid = 0;
       return;
     }
     const int64_t st = p.qs.start[it.s];
@@ -106,18 +100,16 @@ __device__ __forceinline__ int classify_keys(int mask, PosRange k, bool k_bad, i
 }
 
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
   constexpr int QT = kBQ * RB;               // bytes of a Q or dO block tile
   constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
-  constexpr int SST = kBQ + 4;               // dS^T tile row stride (elements): 72 bytes
   // K tile (once), double-buffered Q / dO tiles and LSE / delta rows (loaded
-  // straight from HBM into LDS), and the dS tile of the current block.
+  // straight from HBM into LDS).
   __shared__ __attribute__((aligned(16))) char k_lds[kBK * RB];
   __shared__ __attribute__((aligned(16))) char qd_lds[2][2][QT];          // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kBQ];       // [buffer][lse | delta]
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kBK * SST];       // dS^T [key][query]
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][64];         // [buffer][lse, delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
@@ -186,7 +178,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
 
   // Direct-to-LDS loads of query block b into buffer `buf`: Q and dO rows
   // (rows past the end re-read the last row and are masked) and, from wave
-  // 0, the block's LSE (lanes 0-31) and delta (lanes 32-63).  The per-lane
+  // 0, the block's LSE and delta rows.  The per-lane
   // byte offsets inside a full block are loop invariant.
   constexpr int QLOADS = kBQ / ROWS_PER_LOAD / 4;
   uint32_t qoff[QLOADS];
@@ -196,9 +188,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     qoff[i] = (uint32_t)r * q_row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
   }
   const uint32_t qd_wave = lds_addr(&qd_lds[0][0][0]) + wave * QLOADS * 1024;
-  const uintptr_t lse_row = (uintptr_t)(p.lse + (size_t)h * p.sq);
-  const uintptr_t dlt_row = (uintptr_t)(p.delta + (size_t)h * p.sq);
-  const uintptr_t ld_src = half ? dlt_row : lse_row;    // per lane, from two uniform values
+  const float* lse_h = p.lse + (size_t)h * p.sq;
+  const float* dlt_h = p.delta + (size_t)h * p.sq;
   auto issue = [&](const QIter& b, int buf) {
     const int qr0 = b.qbk * kBQ;
     const uint32_t dst = qd_wave + buf * 2 * QT;
@@ -220,67 +211,36 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
       }
     }
     if (wave == 0) {
-      const uintptr_t src = ld_src + 4 * (uintptr_t)min(qr0 + (lane & 31), p.sq - 1);
-      dma4(reinterpret_cast<const void*>(src), lds_addr(ld_lds[buf]));
+      // lanes l and l + 32 both fetch row qr0 + l (rows past the end: the last row)
+      const uint32_t off = 4u * (uint32_t)min(qr0 + col, p.sq - 1);
+      dma4(lse_h, off, lds_addr(ld_lds[buf][0]));
+      dma4(dlt_h, off, lds_addr(ld_lds[buf][1]));
     }
   };
 
-  // dQ[:, slice] += scale * dS K over the 128 keys of the tile (rows past the
-  // end add 0 to the last row).
-  auto dq_block = [&](int qr0) {
-    constexpr int NDB = D / 32;                    // column slices
-    constexpr int KSPLIT = 4 / NDB;                // waves per slice
-    constexpr int KEYS = kBK / KSPLIT;
-    constexpr int NKS = KEYS / 16;
-    const int wd = wave % NDB, kh = wave / NDB;
-    // operands in groups of 4 k-steps (register budget), two accumulation chains
-    constexpr int G4 = NKS < 4 ? NKS : 4;
-    f32x16 q0 = {}, q1 = {};
-#pragma unroll
-    for (int k0 = 0; k0 < NKS; k0 += G4) {
-      bf16x8 a[G4], b[G4];
-#pragma unroll
-      for (int i = 0; i < G4; ++i) {
-        const int key0 = kh * KEYS + 16 * (k0 + i) + 8 * half;
-        a[i] = tr_operand(ds_lds, SST, key0, key0 + 4, 0, lane);     // dS rows = queries
-        b[i] = tr_operand_swz<CPR>(k_lds, key0, key0 + 4, wd * 32, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < G4; i += 2) {
-        q0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], q0, 0, 0, 0);
-        q1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i + 1], b[i + 1], q1, 0, 0, 0);
-      }
-    }
-    // rows: queries 8*(j/4) + 4*half + j%4; column: d = 32*wd + col.  32-bit
-    // element offsets from the uniform base (dq_acc < 2^32 bytes, checked on
-    // the host).
-    const uint32_t row_stride = (uint32_t)p.hq * D;
-    float* base = p.dq + ((uint32_t)h * D + wd * 32 + col);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qrow = qr0 + 4 * half + 8 * (j >> 2) + (j & 3);
-      const bool ok = qrow < p.sq;
-      unsafeAtomicAdd(base + (uint32_t)(ok ? qrow : p.sq - 1) * row_stride, ok ? (q0[j] + q1[j]) * p.scale : 0.f);
-    }
-  };
+  // Lane offsets inside the tiles: the Q / dO A operands (row `col`), the
+  // K^T B operand (row kr = this wave's key `col`) and the transpose-load
+  // rows 4 * half.. (A part) and 4 * half + 8.. (B part) of k-step t2 = 0
+  // (t2 = 1 is 16 rows further: an immediate offset).
+  const int kr_lane = 32 * wave + col;
+  const uint32_t q_off = row_read_offset<CPR>(col, half);
+  const uint32_t k_off = row_read_offset<CPR>(kr_lane, half);
+  const uint32_t trA = tr_lane_offset<CPR>(4 * half, lane);
+  const uint32_t trB = tr_lane_offset<CPR>(4 * half + 8, lane);
 
-  QIter it{-1, 0, 0, 0, true};
+  QIter it{-1, 0, 0, 0, 1};
   qiter_next(it, p, q_lo, q_hi);
   if (it.valid) issue(it, 0);
-  int buf = 0;
-  int prev_qr0 = -1;      // block whose dS waits in ds_lds for its dQ
-
-  while (it.valid) {
+  // One query block, for a compile-time buffer index (the loop is unrolled
+  // by two so LDS addresses of either buffer are immediate offsets).
+  auto block = [&](auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int qr0 = it.qbk * kBQ;
     const int qr1 = min(qr0 + kBQ, p.sq);
-    // This block's loads have landed (the wait also covers the previous
-    // block's dQ atomics, issued a whole block of compute ago); after the
-    // barrier every wave's loads are visible and the other buffers are free.
+    // This block's loads have landed; after the barrier every wave's loads
+    // are visible and the other buffers are free.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // dQ of the previous block, then the next block's loads: both stay in
-    // flight while this block is computed.
-    if (prev_qr0 >= 0) dq_block(prev_qr0);
     QIter nx = it;
     qiter_next(nx, p, q_lo, q_hi);
     if (nx.valid) issue(nx, buf ^ 1);
@@ -292,21 +252,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     const char* qt = qd_lds[buf][0];
     const char* dot = qd_lds[buf][1];
 
-    f32x16 sacc = {}, dpacc = {};
     if (cls != kSkip) {
+      f32x16 sacc = {}, dpacc = {};
+      const uint32_t qo = opaque(q_off), ko = opaque(k_off);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const int cq = ((2 * ks + half) ^ tile_swz<CPR>(col)) << 4;
-        const int kr = 32 * wave + col;
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + col * RB + cq);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dot + col * RB + cq);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(k_lds + kr * RB + (((2 * ks + half) ^ tile_swz<CPR>(kr)) << 4));
+        const uint32_t oq = qo ^ (ks << 5), okk = ko ^ (ks << 5);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + oq);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dot + oq);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(k_lds + okk);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dpacc, 0, 0, 0);
       }
       // P and dS in place (rows: queries 8*(j/4) + 4*half + j%4; column: my key).
-      const float* lse_b = ld_lds[buf];
-      const float* dlt_b = ld_lds[buf] + kBQ;
+      const float* lse_b = ld_lds[buf][0];
+      const float* dlt_b = ld_lds[buf][1];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int qb0 = 8 * j4 + 4 * half;
@@ -330,6 +290,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
         }
       }
       // dV += P^T dO ; dK += dS^T Q  (k-step t2: queries 16*t2 + ...)
+      const uint32_t ta = opaque(trA), tb = opaque(trB);
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         u32x4 pw, sw;
@@ -340,37 +301,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdParams p) {
         }
         const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
         const bf16x8 sa = __builtin_bit_cast(bf16x8, sw);
-        const int rA = 16 * t2 + 4 * half, rB = rA + 8;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 bdo = tr_operand_swz<CPR>(dot, rA, rB, db * 32, lane);
-          const bf16x8 bq = tr_operand_swz<CPR>(qt, rA, rB, db * 32, lane);
+          const uint32_t oa = ta ^ (db << 6), ob = tb ^ (db << 6);
+          const bf16x8 bdo = tr_read(dot + t2 * 16 * RB, oa, ob);
+          const bf16x8 bq = tr_read(qt + t2 * 16 * RB, oa, ob);
           dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bdo, dvacc[db], 0, 0, 0);
           dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, bq, dkacc[db], 0, 0, 0);
         }
       }
     }
-    // Every wave is past the previous block's dQ: dS (bf16) of this block
-    // replaces it, transposed as ds_lds[key][query] so that each lane's four
-    // consecutive queries are one aligned 8-byte write; skipped waves write
-    // zeros.
-    __syncthreads();
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      u32x2 w = {0u, 0u};
-      if (cls != kSkip) {
-        w[0] = pack_bf16x2(dpacc[4 * j4], dpacc[4 * j4 + 1]);
-        w[1] = pack_bf16x2(dpacc[4 * j4 + 2], dpacc[4 * j4 + 3]);
-      }
-      *reinterpret_cast<u32x2*>(&ds_lds[(32 * wave + col) * SST + 8 * j4 + 4 * half]) = w;
-    }
-    prev_qr0 = qr0;
-    buf ^= 1;
     it = nx;
-  }
-  if (prev_qr0 >= 0) {
-    __syncthreads();
-    dq_block(prev_qr0);
+  };
+  while (it.valid) {
+    block(std::integral_constant<int, 0>{});
+    if (!it.valid) break;
+    block(std::integral_constant<int, 1>{});
   }
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).
@@ -418,12 +364,12 @@ int bwd_keys_per_wg(int d) {
   return kBK;
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t s) {
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s) {
   dim3 grid(p.n_wg), block(kBwdThreads);
   if (d == 128)
-    hipLaunchKernelGGL(bwd_bf16_kernel<128>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, block, 0, s, p);
   else if (d == 64)
-    hipLaunchKernelGGL(bwd_bf16_kernel<64>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

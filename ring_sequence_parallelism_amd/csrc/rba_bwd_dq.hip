@@ -1,0 +1,161 @@
+// Backward ring step, dQ part: dQ_i += scale * sum_j dS_ij k_j over the keys of
+// one KV chunk, with dS_ij = P_ij (<dO_i, v_j> - delta_i) and
+// P_ij = exp(s_ij - LSE_i) from the final merged LSE (the gradient of the
+// softmax attention definition; the pages name training as the workload,
+// HSAP methodology and TASP abstract, but print no backward).
+//
+// gfx950 design: the query-stationary tiling of the forward step.  A
+// workgroup is 4 waves over one KV head; each wave owns 32 query rows of one
+// query head and keeps Q^T and dO^T in registers as MFMA B operands.  K and V
+// tiles of 64 keys stream into double-buffered LDS; each 32-key half of a tile
+// is computed in transposed form (lane = query column) so the softmax-side
+// math stays in-lane:
+//   S^T  = K Q^T      (A: K rows from LDS)
+//   dP^T = V dO^T     (A: V rows from LDS)
+//   P^T  = 2^(scale_log2 s - LSE log2 e),  dS^T = P^T (dP^T - delta)
+//   dQ^T += K^T dS^T  (A: K through the LDS transpose load, B: dS^T packed
+//                      to bf16 in the key order of the accumulator rows)
+// Each (row, head) of dq_acc belongs to one wave: the kernel adds its
+// contribution with one read-modify-write at the end, no atomics.
+#include <type_traits>
+
+#include "rba_qtile.h"
+
+namespace rba {
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams dp) {
+  const FwdParams& p = dp.f;
+  constexpr int CPR = D / 8;
+  constexpr int RB = D * 2;
+  constexpr int TILE = kBN * RB;
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];   // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const WaveTask t = make_task<32>(p, wave);
+  const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
+
+  // Q^T and dO^T as B operands: lane holds query `col`, d = 16*ks + 8*half + 0..7.
+  const int row = t.row0 + col;
+  const bool row_ok = row < p.sq;
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  {
+    const size_t off = ((size_t)(row_ok ? row : 0) * p.hq + t.h) * D;
+    const bf16x8* qs = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(p.q) + off);
+    const bf16x8* ds = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(dp.d_o) + off);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 z = {};
+      qreg[ks] = row_ok ? qs[2 * ks + half] : z;
+      doreg[ks] = row_ok ? ds[2 * ks + half] : z;
+    }
+  }
+  const int32_t qpos = row_ok ? row_to_pos(p.qs, row) : kPosNone;
+  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos) : INT32_MIN;
+  // LSE in base 2 (rows without any allowed key, LSE = -inf, get P = 0 like
+  // rows past the chunk), and delta.
+  float lse2 = INFINITY, dlt = 0.f;
+  if (row_ok) {
+    const float l = dp.lse[(size_t)t.h * p.sq + row];
+    lse2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+    dlt = dp.delta[(size_t)t.h * p.sq + row];
+  }
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
+
+  TileIter it{-1, 0, 0, 0, 1};
+  tile_next(it, p, t);
+  if (it.valid) loader.issue(it.kt, 0);
+  auto tile = [&](auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int kt = it.kt;
+    const int kr0 = kt * kBN;
+    const int kr1 = min(kr0 + kBN, p.sk);
+    // Tile kt has landed for every wave, which are all done with the other buffer.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    TileIter nx = it;
+    tile_next(nx, p, t);
+    if (nx.valid) loader.issue(nx.kt, buf ^ 1);
+
+    const PosRange kr = pos_range(p.ks, kr0, kr1);
+    const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    if (cls != kSkip) {
+      const char* kt_lds = lds[buf][0];
+      const char* vt_lds = lds[buf][1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T and dP^T for keys kb*32 .. +31 (rows of the A operands).
+        f32x16 sacc = {}, dpacc = {};
+        const int r = kb * 32 + col;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int c = ((2 * ks + half) ^ tile_swz<CPR>(r)) << 4;
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt_lds + r * RB + c);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt_lds + r * RB + c);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dpacc, 0, 0, 0);
+        }
+        if (cls == kPartial) mask_block(sacc, p, kr, kr0, kb, half, qpos, qds);
+        // dS^T in place, packed to bf16 pairs in accumulator order.
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(fmaf(sacc[2 * i], p.scale_log2, -lse2));
+          const float p1 = fast_exp2(fmaf(sacc[2 * i + 1], p.scale_log2, -lse2));
+          w[i] = pack_bf16x2(p0 * (dpacc[2 * i] - dlt), p1 * (dpacc[2 * i + 1] - dlt));
+        }
+        // dQ^T += K^T dS^T.  k-slot of dS^T register j <-> key
+        // 16*t2 + 8*(i/4) + 4*half + i%4 (as P^T in the forward's PV).
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 wv = {w[4 * t2], w[4 * t2 + 1], w[4 * t2 + 2], w[4 * t2 + 3]};
+          const bf16x8 b = __builtin_bit_cast(bf16x8, wv);
+          const int rA = kb * 32 + 16 * t2 + 4 * half;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = tr_operand_swz<CPR>(kt_lds, rA, rA + 8, db * 32, lane);
+            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dqacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    it = nx;
+  };
+  while (it.valid) {
+    tile(std::integral_constant<int, 0>{});
+    if (!it.valid) break;
+    tile(std::integral_constant<int, 1>{});
+  }
+
+  // dq_acc[row, h, :] += scale * dQ^T[:, row] (accumulator rows: d =
+  // 32*db + 8*(j/4) + 4*half + j%4, four consecutive d per f32x4).
+  if (row_ok) {
+    float* dst = dp.dq + ((size_t)row * p.hq + t.h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4* q4 = reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half);
+        const f32x4 add = {dqacc[db][4 * jj], dqacc[db][4 * jj + 1], dqacc[db][4 * jj + 2], dqacc[db][4 * jj + 3]};
+        *q4 = *q4 + add * dp.scale;
+      }
+  }
+}
+
+hipError_t launch_bwd_dq(const DqParams& p, int d, hipStream_t s) {
+  dim3 grid(p.f.n_wg), block(kThreads);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, block, 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, block, 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace rba

@@ -185,6 +185,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Per-lane byte offsets into a swizzled, unpadded tile for the XOR-linear
+// swizzle (the chunk and column-block terms below occupy bits that the row
+// term leaves clear, so XOR equals addition there):
+//  * row_read_offset: the 16-byte chunk (2 * ks + half) of tile row `row` is
+//    at row_read_offset(row, half) ^ (ks << 5).
+//  * tr_lane_offset: the transpose-load operand rows row.. row + 3 (source
+//    lane j: row + j / 4, column 16 * ((lane >> 4) & 1) + 4 * (j % 4), see
+//    tr_operand) at column block 0; column block db (32 * db elements) is
+//    at tr_lane_offset(row, lane) ^ (db << 6).
+template <int CPR>
+__device__ __forceinline__ uint32_t row_read_offset(int row, int half) {
+  return (uint32_t)row * (CPR * 16) + ((uint32_t)(half ^ tile_swz<CPR>(row)) << 4);
+}
+template <int CPR>
+__device__ __forceinline__ uint32_t tr_lane_offset(int row, int lane) {
+  const int j = lane & 15;
+  const int colx = 16 * ((lane >> 4) & 1) + 4 * (j & 3);   // element column in block 0
+  const int ra = row + (j >> 2);
+  return (uint32_t)ra * (CPR * 16) + ((uint32_t)((colx >> 3) ^ tile_swz<CPR>(ra)) << 4) + (colx & 7) * 2;
+}
+
+// The transpose-load operand whose two row groups sit at byte addresses
+// base + offA and base + offB (k-slots 0..3 and 4..7 of the lane's half).
+__device__ __forceinline__ bf16x8 tr_read(const char* base, uint32_t offA, uint32_t offB) {
+  typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(base + offA));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(base + offB));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Keeps the compiler from hoisting work derived from `x` out of a loop (no
+// instruction is emitted): used on lane offsets so that per-iteration XORs
+// are recomputed instead of occupying registers for the whole loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Direct-to-LDS load, 16 bytes per lane, in the scalar-base form: lane l
 // reads global address sbase + voff (voff a 32-bit byte offset) and its data
 // lands at LDS byte address lds + 16 * l.  sbase and lds must be uniform
@@ -222,20 +262,21 @@ __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint3
       : "memory");
 }
 
-// Direct-to-LDS load of 4 bytes per lane from a per-lane 64-bit address;
-// lane l's dword lands at LDS byte address lds + 4 * l (lds uniform).  Same
-// ordering contract as dma16.
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_in) {
+// Direct-to-LDS load of 4 bytes per lane in the scalar-base form: lane l
+// reads sbase + voff and its dword lands at LDS byte address lds + 4 * l
+// (sbase, lds uniform).  Same ordering contract as dma16.
+__device__ __forceinline__ void dma4(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
+  const char* sbase = uniform_ptr(sbase_in);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
+      "global_load_lds_dword %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(gptr), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 

@@ -31,108 +31,9 @@
 //     and a lazy running maximum that rarely rescales O.
 #include <type_traits>
 
-#include "rba_device.h"
+#include "rba_qtile.h"
 
 namespace rba {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBN = 64;  // keys per tile
-
-// Setup shared by both element types: which rows/head this wave owns and the
-// allowed key interval of the workgroup.
-struct WaveTask {
-  int g, h, row0;           // kv head, query head, first row of the wave
-  int wg_row0, wg_rows;     // workgroup row range
-  bool wave_any;            // the wave has at least one valid row
-  int32_t wq_lo, wq_hi;     // wave query position range
-  int32_t wds_lo, wds_hi;   // document starts of wq_lo / wq_hi (doc mask)
-  int64_t k_lo, k_hi;       // allowed key positions for the workgroup
-};
-
-template <int QR>
-__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave) {
-  const int logical = xcd_remap(blockIdx.x, p.n_wg);
-  const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
-  const int rg = logical % p.n_row_groups;
-  WaveTask t;
-  const int hw = wave % p.hpw, rb = wave / p.hpw;
-  t.h = hg * p.hpw + hw;
-  t.g = t.h / p.group;
-  t.wg_row0 = rg * p.rbw * QR;
-  t.wg_rows = min(p.rbw * QR, p.sq - t.wg_row0);
-  t.row0 = t.wg_row0 + rb * QR;
-  const int wr1 = min(t.row0 + QR, p.sq);
-  t.wave_any = t.row0 < wr1;
-  t.wq_lo = INT32_MAX; t.wq_hi = INT32_MIN; t.wds_lo = INT32_MIN; t.wds_hi = INT32_MIN;
-  if (t.wave_any) {
-    PosRange r = pos_range(p.qs, t.row0, wr1);
-    t.wq_lo = r.lo; t.wq_hi = r.hi;
-    if (p.mask == kMaskDoc) {
-      t.wds_lo = doc_start(p.cu, p.n_docs, r.lo);
-      t.wds_hi = doc_start(p.cu, p.n_docs, r.hi);
-    }
-  }
-  PosRange wr = pos_range(p.qs, t.wg_row0, t.wg_row0 + t.wg_rows);
-  t.k_lo = kPosNegInf; t.k_hi = kPosPosInf;
-  if (p.mask != kMaskNone) t.k_hi = wr.hi;
-  if (p.mask == kMaskDoc) t.k_lo = doc_start(p.cu, p.n_docs, wr.lo);
-  return t;
-}
-
-// Visits, in row order, every key tile that may hold an allowed key for the
-// workgroup: for each KV segment, the rows whose positions fall in
-// [k_lo, k_hi].  `body(kt)` is called once per tile.
-template <typename F>
-__device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask& t, F&& body) {
-  int next_tile = 0;
-  for (int s = 0; s < p.ks.n; ++s) {
-    const int64_t st = p.ks.start[s];
-    const int r0 = p.ks.row0[s];
-    const int64_t len = p.ks.row0[s + 1] - r0;
-    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
-    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
-    if (a >= b) continue;
-    const int t0 = max((int)((r0 + a) / kBN), next_tile);
-    const int t1 = (int)((r0 + b + kBN - 1) / kBN);
-    for (int kt = t0; kt < t1; ++kt) body(kt);
-    next_tile = max(next_tile, t1);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16
-
-// Iterator over the key tiles for_each_tile visits (same order), so that the
-// next tile's loads can be issued before the current tile is computed.
-struct TileIter {
-  int s, kt, t1, next_tile;
-  int valid;   // int, not bool: a padding-free struct stays in registers
-};
-
-__device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, const WaveTask& t) {
-  ++it.kt;
-  while (it.kt >= it.t1) {
-    ++it.s;
-    if (it.s >= p.ks.n) {
-      it.valid = 0;
-      return;
-    }
-    const int64_t st = p.ks.start[it.s];
-    const int r0 = p.ks.row0[it.s];
-    const int64_t len = p.ks.row0[it.s + 1] - r0;
-    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
-    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
-    if (a >= b) {
-      it.kt = 0;
-      it.t1 = 0;
-      continue;
-    }
-    it.kt = max((int)((r0 + a) / kBN), it.next_tile);
-    it.t1 = (int)((r0 + b + kBN - 1) / kBN);
-    it.next_tile = max(it.next_tile, it.t1);
-  }
-}
 
 template <int D, int NQB>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
@@ -140,8 +41,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RB = D * 2;                  // bytes per row (no padding: swizzled)
   constexpr int TILE = kBN * RB;             // bytes per K or V tile
-  constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
-  constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;   // per wave per tensor per tile
   // [buffer][K, V] tiles, double-buffered: tile t is computed from buffer t % 2
   // while tile t + 1 streams into the other one.
   __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];
@@ -150,9 +49,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
   const int col = lane & 31, half = lane >> 5;
   const WaveTask t = make_task<QR>(p, wave);
-  const uint32_t row_bytes = (uint32_t)p.hkv * RB;     // stride of a K/V row in global memory
-  const char* kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(t.g * RB));
-  const char* vg = uniform_ptr(static_cast<const char*>(p.v) + (uint32_t)(t.g * RB));
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -172,43 +68,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     qds[qb] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
   }
 
-  // Direct-to-LDS loads of key tile kt into buffer b.  Load i of this wave
-  // fills tile rows (wave * LOADS + i) * ROWS_PER_LOAD + lane / CPR: lane l
-  // writes chunk position l % CPR of its row and fetches the global chunk that
-  // the swizzle stores there.  The per-lane byte offsets inside a tile are
-  // loop invariant and a tile adds a uniform base; in the last, ragged tile,
-  // lanes whose row is past the end of the chunk step back to its last row
-  // (finite values, masked out).
-  // Lane offsets: load i covers rows r_lane + ROWS_PER_LOAD * i, where the
-  // two terms share no set bit (r_lane = 16 * wave + lane / 16 for d = 128,
-  // 16 * wave + lane / 8 for d = 64), so its row term is a uniform step of
-  // load 0's and, tile_swz being XOR-linear, its swizzled chunk is load 0's
-  // XOR tile_swz(ROWS_PER_LOAD * i).
-  static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile rows");
-  const int r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;      // row of load 0
-  const uint32_t loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
-  auto chunk_xor = [](int i) -> uint32_t { return (uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4; };
-  const uint32_t lds_wave = lds_addr(&lds[0][0][0]) + wave * LOADS * 1024;
-  auto issue = [&](int kt, int b) {
-    const uint32_t dst = lds_wave + b * 2 * TILE;
-    const bool whole = (kt + 1) * kBN <= p.sk;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      size_t tb = ((size_t)kt * kBN + i * ROWS_PER_LOAD) * row_bytes;
-      uint32_t off = loff0 ^ chunk_xor(i);
-      if (!whole) {
-        // Relative to the tile's first row: the clamped row is at or past
-        // it, so the unsigned lane offset never wraps (load i's own first
-        // row may lie past the end of the chunk).
-        tb = (size_t)kt * kBN * row_bytes;
-        off += (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
-        const int over = kt * kBN + r_lane + i * ROWS_PER_LOAD - (p.sk - 1);
-        if (over > 0) off -= (uint32_t)over * row_bytes;
-      }
-      dma16(kg + tb, off, dst + i * 1024);
-      dma16(vg + tb, off, dst + TILE + i * 1024);
-    }
-  };
+  const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
 
   f32x16 oacc[NQB][D / 32];
   float m_run[NQB], l_run[NQB];
@@ -222,7 +82,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   TileIter it{-1, 0, 0, 0, 1};
   tile_next(it, p, t);
-  if (it.valid) issue(it.kt, 0);
+  if (it.valid) loader.issue(it.kt, 0);
   // The body of one key tile, for a compile-time buffer index (the loop is
   // unrolled by two so LDS addresses of either buffer are immediate offsets).
   auto tile = [&](auto buf_c) {
@@ -236,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     TileIter nx = it;
     tile_next(nx, p, t);
-    if (nx.valid) issue(nx.kt, buf ^ 1);
+    if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
     const PosRange kr = pos_range(p.ks, kr0, kr1);
     const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
@@ -263,32 +123,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       }
 
       if (cls == kPartial) {
-        // Key positions of this lane's 32 accumulator rows.  Every element is
-        // rewritten through a select (no conditional stores into the vectors).
-        int32_t kp[2][16];
-        if (kr.single) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        } else {
-          for (int kb = 0; kb < 2; ++kb)
-            for (int j = 0; j < 16; ++j) {
-              const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-              kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
-            }
-        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-              const bool ok = kin && visible(p.mask, kp[kb][j], qpos[qb], qds[qb]);
-              sacc[kb][qb][j] = ok ? sacc[kb][qb][j] : -INFINITY;
-            }
-          }
+          for (int qb = 0; qb < NQB; ++qb) mask_block(sacc[kb][qb], p, kr, kr0, kb, half, qpos[qb], qds[qb]);
       }
 
       // Online softmax (base 2) per query column with a lazy maximum: the

@@ -236,6 +236,30 @@ int prepare_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t 
   return RBA_OK;
 }
 
+// Sizes, mask, segments and the launch geometry of the query-stationary
+// kernels (forward step, backward dQ): workgroups of 4 waves, each wave
+// `rows_per_wave` query rows of one head; a workgroup takes 4, 2 or 1 query
+// heads of one KV head (hpw) times 1, 2 or 4 row blocks (rbw).
+int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan& plan, int rows_per_wave,
+                      rba::FwdParams& p) {
+  p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.mask = a->mask;
+  p.cu = a->mask == RBA_MASK_DOC_CAUSAL ? a->cu_seqlens_dev : nullptr;
+  p.n_docs = a->mask == RBA_MASK_DOC_CAUSAL ? a->n_docs : 0;
+  p.qs = to_table(plan.qs);
+  p.ks = to_table(plan.ks);
+  p.hpw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0 ? 2 : 1);
+  p.rbw = 4 / p.hpw;
+  const int64_t rows_per_wg = (int64_t)p.rbw * rows_per_wave;
+  p.n_row_groups = (int32_t)((sq + rows_per_wg - 1) / rows_per_wg);
+  p.n_head_groups = a->hq / p.hpw;
+  const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
+  if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
+  p.n_wg = (int32_t)n_wg;
+  return RBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,22 +298,7 @@ int rba_fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
 
   rba::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o_part; p.lse = lse_part;
-  p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
-  p.scale_log2 = a->scale * 1.4426950408889634f;
-  p.mask = a->mask;
-  p.cu = a->mask == RBA_MASK_DOC_CAUSAL ? a->cu_seqlens_dev : nullptr;
-  p.n_docs = a->mask == RBA_MASK_DOC_CAUSAL ? a->n_docs : 0;
-  p.qs = to_table(plan.qs);
-  p.ks = to_table(plan.ks);
-  p.hpw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0 ? 2 : 1);
-  p.rbw = 4 / p.hpw;
-  const int qr = rba::fwd_rows_per_wave(a->d, bf16);
-  const int64_t rows_per_wg = (int64_t)p.rbw * qr;
-  p.n_row_groups = (int32_t)((sq + rows_per_wg - 1) / rows_per_wg);
-  p.n_head_groups = a->hq / p.hpw;
-  const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
-  if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
-  p.n_wg = (int32_t)n_wg;
+  if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, bf16), p))) return rc;
   hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
   return hip_status(e, "forward step");
 }
@@ -352,15 +361,15 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
       (rc = check_ptr(dq_acc, "dq_acc")) || (rc = check_ptr(dk_step, "dk_step")) ||
       (rc = check_ptr(dv_step, "dv_step")))
     return rc;
-  if ((int64_t)sq * a->hq * a->d * 4 >= ((int64_t)1 << 32))
-    return fail(RBA_ERR_UNSUPPORTED, "backward step: dq_acc must be smaller than 4 GiB");
+  if ((int64_t)sq * a->hq * a->d * 2 >= ((int64_t)1 << 32))
+    return fail(RBA_ERR_UNSUPPORTED, "backward step: q and d_o must each be smaller than 4 GiB");
   if (sk * a->hkv * a->d * 2 >= ((int64_t)1 << 32))
     return fail(RBA_ERR_UNSUPPORTED, "backward step: k and v must each be smaller than 4 GiB");
   if (plan.empty) return RBA_STEP_EMPTY;
   if ((rc = check_device())) return rc;
   rba::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.d_o = d_o; p.lse = lse; p.delta = delta;
-  p.dq = dq_acc; p.dk = dk_step; p.dv = dv_step;
+  p.dk = dk_step; p.dv = dv_step;
   p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
@@ -379,7 +388,13 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
     hipError_t e = rba::launch_zero_f32(dk_step, dv_step, sk * a->hkv * a->d, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "backward zero fill");
   }
-  return hip_status(rba::launch_bwd_bf16(p, a->d, (hipStream_t)stream), "backward step");
+  hipError_t e = rba::launch_bwd_dkdv(p, a->d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "backward step (dK, dV)");
+  rba::DqParams dp{};
+  dp.f.q = q; dp.f.k = k; dp.f.v = v;
+  if ((rc = fill_query_tiling(a, sq, sk, plan, 32, dp.f))) return rc;
+  dp.d_o = d_o; dp.lse = lse; dp.delta = delta; dp.dq = dq_acc; dp.scale = a->scale;
+  return hip_status(rba::launch_bwd_dq(dp, a->d, (hipStream_t)stream), "backward step (dQ)");
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@ struct FwdParams {
   int32_t n_wg;
 };
 
-// Backward step.
+// Backward step, dK / dV kernel (key-stationary).
 struct BwdParams {
   const void* q;
   const void* k;
@@ -48,7 +48,6 @@ struct BwdParams {
   const void* d_o;
   const float* lse;    // [hq, sq] final log-sum-exp (natural log)
   const float* delta;  // [hq, sq]
-  float* dq;           // [sq, hq, d] accumulated with atomics
   float* dk;           // [sk, hkv, d] overwritten
   float* dv;           // [sk, hkv, d] overwritten
   int32_t sq, sk, hq, hkv, group;
@@ -60,6 +59,17 @@ struct BwdParams {
   SegTable qs, ks;
   int32_t n_key_tiles;
   int32_t n_wg;      // n_key_tiles * hkv * group: one workgroup per (key tile, query head)
+};
+
+// Backward dQ kernel: the query-stationary geometry of a forward step (the
+// o and lse members of `f` are unused) plus the backward operands.
+struct DqParams {
+  FwdParams f;
+  const void* d_o;     // [sq, hq, d] bf16
+  const float* lse;    // [hq, sq] final log-sum-exp (natural log)
+  const float* delta;  // [hq, sq]
+  float* dq;           // [sq, hq, d] fp32, dq += scale * dS K
+  float scale;
 };
 
 struct MergeParams {
@@ -87,7 +97,8 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dq(const DqParams& p, int d, hipStream_t s);
 hipError_t launch_zero_f32(float* a, float* b, int64_t n, hipStream_t s);
 
 // Rows of the forward workgroup tile per wave (32 * fwd_row_blocks).

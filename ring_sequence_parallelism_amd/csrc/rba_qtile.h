@@ -1,0 +1,194 @@
+// Query-stationary tiling shared by the forward step and the backward dQ
+// kernel: a workgroup of 4 waves owns query rows of one or more query heads
+// that share a KV head, and walks the key tiles that may hold an allowed key
+// for its rows.
+#pragma once
+
+#include "rba_device.h"
+
+namespace rba {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;  // keys per tile
+
+// Which rows and head a wave owns, and the
+// allowed key interval of the workgroup.
+struct WaveTask {
+  int g, h, row0;           // kv head, query head, first row of the wave
+  int wg_row0, wg_rows;     // workgroup row range
+  bool wave_any;            // the wave has at least one valid row
+  int32_t wq_lo, wq_hi;     // wave query position range
+  int32_t wds_lo, wds_hi;   // document starts of wq_lo / wq_hi (doc mask)
+  int64_t k_lo, k_hi;       // allowed key positions for the workgroup
+};
+
+template <int QR>
+__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave) {
+  const int logical = xcd_remap(blockIdx.x, p.n_wg);
+  const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
+  const int rg = logical % p.n_row_groups;
+  WaveTask t;
+  const int hw = wave % p.hpw, rb = wave / p.hpw;
+  t.h = hg * p.hpw + hw;
+  t.g = t.h / p.group;
+  t.wg_row0 = rg * p.rbw * QR;
+  t.wg_rows = min(p.rbw * QR, p.sq - t.wg_row0);
+  t.row0 = t.wg_row0 + rb * QR;
+  const int wr1 = min(t.row0 + QR, p.sq);
+  t.wave_any = t.row0 < wr1;
+  t.wq_lo = INT32_MAX; t.wq_hi = INT32_MIN; t.wds_lo = INT32_MIN; t.wds_hi = INT32_MIN;
+  if (t.wave_any) {
+    PosRange r = pos_range(p.qs, t.row0, wr1);
+    t.wq_lo = r.lo; t.wq_hi = r.hi;
+    if (p.mask == kMaskDoc) {
+      t.wds_lo = doc_start(p.cu, p.n_docs, r.lo);
+      t.wds_hi = doc_start(p.cu, p.n_docs, r.hi);
+    }
+  }
+  PosRange wr = pos_range(p.qs, t.wg_row0, t.wg_row0 + t.wg_rows);
+  t.k_lo = kPosNegInf; t.k_hi = kPosPosInf;
+  if (p.mask != kMaskNone) t.k_hi = wr.hi;
+  if (p.mask == kMaskDoc) t.k_lo = doc_start(p.cu, p.n_docs, wr.lo);
+  return t;
+}
+
+// Visits, in row order, every key tile that may hold an allowed key for the
+// workgroup: for each KV segment, the rows whose positions fall in
+// [k_lo, k_hi].  `body(kt)` is called once per tile.
+template <typename F>
+__device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask& t, F&& body) {
+  int next_tile = 0;
+  for (int s = 0; s < p.ks.n; ++s) {
+    const int64_t st = p.ks.start[s];
+    const int r0 = p.ks.row0[s];
+    const int64_t len = p.ks.row0[s + 1] - r0;
+    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
+    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    if (a >= b) continue;
+    const int t0 = max((int)((r0 + a) / kBN), next_tile);
+    const int t1 = (int)((r0 + b + kBN - 1) / kBN);
+    for (int kt = t0; kt < t1; ++kt) body(kt);
+    next_tile = max(next_tile, t1);
+  }
+}
+
+// Iterator over the key tiles for_each_tile visits (same order), so that the
+// next tile's loads can be issued before the current tile is computed.
+struct TileIter {
+  int s, kt, t1, next_tile;
+  int valid;   // int, not bool: a padding-free struct stays in registers
+};
+
+__device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, const WaveTask& t) {
+  ++it.kt;
+  while (it.kt >= it.t1) {
+    ++it.s;
+    if (it.s >= p.ks.n) {
+      it.valid = 0;
+      return;
+    }
+    const int64_t st = p.ks.start[it.s];
+    const int r0 = p.ks.row0[it.s];
+    const int64_t len = p.ks.row0[it.s + 1] - r0;
+    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
+    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    if (a >= b) {
+      it.kt = 0;
+      it.t1 = 0;
+      continue;
+    }
+    it.kt = max((int)((r0 + a) / kBN), it.next_tile);
+    it.t1 = (int)((r0 + b + kBN - 1) / kBN);
+    it.next_tile = max(it.next_tile, it.t1);
+  }
+}
+
+// Direct-to-LDS loads of K and V key tiles (kBN rows of one KV head) into
+// double-buffered LDS tiles of unpadded, swizzled rows: [buffer][K, V][tile].
+// Load i of a wave fills tile rows (wave * LOADS + i) * ROWS_PER_LOAD +
+// lane / CPR: lane l writes chunk position l % CPR of its row and fetches the
+// global chunk that the swizzle stores there.  Load i covers rows r_lane +
+// ROWS_PER_LOAD * i, where the two terms share no set bit (r_lane = 16 * wave
+// + lane / 16 for d = 128, 16 * wave + lane / 8 for d = 64), so its row term
+// is a uniform step of load 0's and, tile_swz being XOR-linear, its swizzled
+// chunk is load 0's XOR tile_swz(ROWS_PER_LOAD * i): the per-lane offsets are
+// one loop-invariant register and a tile adds a uniform base.  In the last,
+// ragged tile, lanes whose row is past the end of the chunk step back to its
+// last row (finite values, masked out).
+template <int D>
+struct KvLoader {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RB = D * 2;                  // bytes per tile row
+  static constexpr int TILE = kBN * RB;             // bytes per K or V tile
+  static constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
+  static constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;   // per wave per tensor per tile
+  static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile rows");
+
+  const char* kg;       // K and V rows of the KV head (uniform)
+  const char* vg;
+  uint32_t row_bytes;   // stride of a K/V row in global memory
+  int sk, r_lane;
+  uint32_t loff0;       // lane offset of load 0 inside a tile
+  uint32_t lds_wave;    // LDS byte address of this wave's part of buffer 0's K tile
+
+  __device__ __forceinline__ KvLoader(const FwdParams& p, int g, int wave, int lane, uint32_t lds_base) {
+    row_bytes = (uint32_t)p.hkv * RB;
+    kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(g * RB));
+    vg = uniform_ptr(static_cast<const char*>(p.v) + (uint32_t)(g * RB));
+    sk = p.sk;
+    r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;
+    loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
+    lds_wave = lds_base + wave * LOADS * 1024;
+  }
+
+  // Loads key tile kt into buffer b.
+  __device__ __forceinline__ void issue(int kt, int b) const {
+    const uint32_t dst = lds_wave + b * 2 * TILE;
+    const bool whole = (kt + 1) * kBN <= sk;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      size_t tb = ((size_t)kt * kBN + i * ROWS_PER_LOAD) * row_bytes;
+      uint32_t off = loff0 ^ ((uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4);
+      if (!whole) {
+        // Relative to the tile's first row: the clamped row is at or past
+        // it, so the unsigned lane offset never wraps (load i's own first
+        // row may lie past the end of the chunk).
+        tb = (size_t)kt * kBN * row_bytes;
+        off += (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
+        const int over = kt * kBN + r_lane + i * ROWS_PER_LOAD - (sk - 1);
+        if (over > 0) off -= (uint32_t)over * row_bytes;
+      }
+      dma16(kg + tb, off, dst + i * 1024);
+      dma16(vg + tb, off, dst + TILE + i * 1024);
+    }
+  }
+};
+
+// Sets to -inf the elements of a 32-key block of an S^T accumulator (keys of
+// tile rows kb * 32 .. + 31, this lane's query at position qpos with document
+// start qd) that the mask does not allow, or that lie past the chunk.  Lane
+// (col, half) holds keys kb * 32 + 8 * (j / 4) + 4 * half + j % 4 in element
+// j.  Every element is rewritten through a select (no conditional stores
+// into the vector).
+__device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const PosRange& kr, int kr0, int kb,
+                                           int half, int32_t qpos, int32_t qd) {
+  int32_t kp[16];
+  if (kr.single) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kp[j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+  } else {
+    for (int j = 0; j < 16; ++j) {
+      const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+      kp[j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
+    const bool ok = kin && visible(p.mask, kp[j], qpos, qd);
+    s[j] = ok ? s[j] : -INFINITY;
+  }
+}
+
+}  // namespace rba
