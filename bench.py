@@ -44,7 +44,22 @@ def parse():
                     help="also time the forward replays of the 64K packed-document and 512K zigzag workloads")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows in the CPU-oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 4 device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n * 4, "launches": 4}), flush=True)
 
 
 class LaunchTimer:
@@ -67,6 +82,33 @@ class LaunchTimer:
         for (kind, i, a), (_, _, b) in zip(self.marks[:-1], self.marks[1:]):
             out.append((kind, i, a.elapsed_time(b)))
         return out
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bwd_step_32k_zigzag_hbm_traffic.md")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    src = os.path.join(ROOT, "ring_sequence_parallelism_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(f for f in os.listdir(src) if f.endswith((".hip", ".h", ".cpp"))):
+        h.update(f.encode())
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per rba_bwd_step from the committed rocprofv3 counter summary,
+    or None when the kernel sources changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(l.split(": ", 1) for l in f.read().splitlines() if l.startswith(("traffic_", "sources_")))
+        if kv["sources_sha256"].strip() != kernel_sources_sha256():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def run_step(rr, timer=None):
@@ -107,6 +149,9 @@ def cpu_baseline(w, rows_n):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the ring is replayed on a single MI355X "
               f"(got --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
@@ -164,8 +209,10 @@ def main():
     dk = kern[dom]
     achieved = dk["work"] / (dk["total_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "rba_bwd_step" if dom == "bwd" else "rba_fwd_step",
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic() if dom == "bwd" else None,
+                "kernel": ("rba_bwd_step (dK/dV zero fill, dK/dV and dQ kernels)" if dom == "bwd"
+                           else "rba_fwd_step"),
                 "avg_launch_us": round(dk["avg_us"], 2)}
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     fwd_t = kern["fwd"]["work"] / (kern["fwd"]["total_ms"] * 1e-3) / 1e12
