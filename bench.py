@@ -230,6 +230,25 @@ def main():
     }
     extra = {}
     if args.extra:
+        # the same 32K zigzag forward under TASP's decomposed schedule: steps
+        # are unions of 7 slices from different source ranks
+        from ring_sequence_parallelism_amd.ring import TaspReplay
+        tx = TaspReplay(W.WORKLOADS["c2"], None, "cuda")
+        tx.forward()
+        torch.cuda.synchronize()
+        tm = LaunchTimer(torch)
+        for _ in range(3):
+            tx.forward(on_step=tm)
+        tm.close()
+        torch.cuda.synchronize()
+        f_ms = sum(ms for kind, _, ms in tm.durations() if kind == "fwd") / 3
+        m_ms = sum(ms for kind, _, ms in tm.durations() if kind == "merge") / 3
+        t = tx.fwd_flops() / (f_ms * 1e-3) / 1e12
+        extra["c2_tasp_schedule_fwd"] = {"fwd_step_tflops": round(t, 2), "frac_peak": round(t / PEAK_BF16_TFLOPS, 4),
+                                         "fwd_ms": round(f_ms, 3), "merge_ms": round(m_ms, 3),
+                                         "max_segments_per_step": max(tx.kv_segs[i].n for i in tx.kv_segs)}
+        del tx
+        torch.cuda.empty_cache()
         for key in ("c3", "c4"):
             wx = W.WORKLOADS[key]
             ranks = range(wx.n_ranks) if key == "c3" else [wx.rank]

@@ -58,10 +58,8 @@ class RingReplay:
         srcs = sorted(set(self.order if kv_sources is None else kv_sources))
         # inputs
         self.q = to_device(W.gen_rank_chunk(w, W.T_Q, self.r), w.dtype, self.device)
-        self.k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in srcs}
-        self.v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in srcs}
         self.q_segs = rba.make_segs(w.rank_segments(self.r))
-        self.kv_segs = {j: rba.make_segs(w.rank_segments(j)) for j in srcs}
+        self.order = self._build_kv(srcs)
         self.cu_host = None
         self.cu_dev = None
         if w.mask == W.MASK_DOC_CAUSAL:
@@ -93,6 +91,15 @@ class RingReplay:
             self.dq = torch.empty((sq, hq, d), **f32)
             self.dk = {s.src: torch.empty((self.k[s.src].shape[0], w.hkv, d), **f32) for s in self.steps}
             self.dv = {s.src: torch.empty((self.k[s.src].shape[0], w.hkv, d), **f32) for s in self.steps}
+
+    def _build_kv(self, srcs):
+        """Device K / V and segments of every step, keyed as the steps are;
+        returns the step keys in replay order."""
+        w = self.w
+        self.k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in srcs}
+        self.v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in srcs}
+        self.kv_segs = {j: rba.make_segs(w.rank_segments(j)) for j in srcs}
+        return self.order
 
     # -- forward -----------------------------------------------------------
     @property
@@ -169,3 +176,41 @@ class RingReplay:
                                   self.dq, self.dk[s.src], self.dv[s.src], stream)
             assert st == rba.RBA_OK
         return self.dq, self.dk, self.dv
+
+
+class TaspReplay(RingReplay):
+    """One rank's ring under TASP's decomposed schedule (see tasp.py).
+
+    Iteration 0 is the rank's own chunk; iteration s >= 1 is the union of the
+    n - 1 slices the rank holds then, one per Hamiltonian cycle, assembled in
+    cycle order into one KV buffer (standing in for the receive buffer the
+    transfers would fill) and passed to rba_fwd_step / rba_bwd_step with the
+    slices' position segments.  Steps are keyed by iteration: ``k[s]``,
+    ``v[s]``, ``kv_segs[s]``, ``dk[s]``, ``dv[s]`` and ``slices[s]``.
+    """
+
+    def __init__(self, w: W.Workload, rank: Optional[int] = None, device="cuda", with_grad: bool = False,
+                 schedule=None):
+        from . import tasp
+        self.schedule = schedule if schedule is not None else tasp.TaspSchedule(w.n_ranks)
+        if self.schedule.n != w.n_ranks:
+            raise ValueError("schedule is for a different number of ranks")
+        r = w.rank if rank is None else rank
+        self.slices = [self.schedule.step_slices(r, it, w.chunk_len) for it in range(w.n_ranks)]
+        segs = [tasp.step_segments(w, sl) for sl in self.slices]
+        if max(len(x) for x in segs) > rba.RBA_MAX_SEGS:
+            raise ValueError("a step has more position segments than rba_segs holds")
+        self._tasp_segs = segs
+        super().__init__(w, r, device, kv_sources=None, with_grad=with_grad)
+
+    def _build_kv(self, srcs):
+        w = self.w
+        chunk_k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in range(w.n_ranks)}
+        chunk_v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in range(w.n_ranks)}
+        self.k, self.v, self.kv_segs = {}, {}, {}
+        for it, sl in enumerate(self.slices):
+            self.k[it] = torch.cat([chunk_k[x.src][x.rows[0]:x.rows[1]] for x in sl]).contiguous()
+            self.v[it] = torch.cat([chunk_v[x.src][x.rows[0]:x.rows[1]] for x in sl]).contiguous()
+            self.kv_segs[it] = rba.make_segs(self._tasp_segs[it])
+        del chunk_k, chunk_v
+        return list(range(w.n_ranks))
