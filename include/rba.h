@@ -173,6 +173,25 @@ int rba_bwd_step(const rba_attn* a,
                  float* dq_acc, float* dk_step, float* dv_step, void* stream);
 
 /*
+ * rba_bwd_step_acc — rba_bwd_step with the KV side accumulated: the step's
+ * dK / dV are ADDED into dk_acc / dv_acc [sk, hkv, d] fp32 (in/out) instead
+ * of overwriting per-step outputs.  In a ring, these are the gradient
+ * accumulators that travel with a KV chunk back to its owner (every rank
+ * whose queries meet the chunk adds its part, as the backward of the
+ * attention definition sums dK_j, dV_j over all queries; TASP abstract,
+ * training in HSAP methodology).  No zero fill is launched.  Same arguments,
+ * layouts, limits and errors as rba_bwd_step; on RBA_STEP_EMPTY nothing is
+ * launched and the accumulators are unchanged.  With more than one query
+ * head per KV head the additions are fp32 atomics (low bits depend on
+ * scheduling); with one, each element is read, added and written once.
+ */
+int rba_bwd_step_acc(const rba_attn* a,
+                     const void* q, int64_t sq, const rba_segs* q_segs,
+                     const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                     const void* d_o, const float* lse, const float* delta,
+                     float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
+
+/*
  * rba_plan_step — host-only planning of a step (no device access).
  * Writes into *pairs the exact number of allowed (query row, key) pairs of
  * the step per query head (the effective work: forward 4*d flops per pair

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).
   // With one query head per KV head the workgroup owns its keys' gradients
-  // and stores them; otherwise the group's workgroups add into zeroed outputs.
+  // and stores (or adds) them; otherwise the group's workgroups add with
+  // atomics, into zeroed outputs or into the accumulators.
   if (!wave_any) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -331,9 +332,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
       if (krow < p.sk) {
         float* dkp = p.dk + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
         float* dvp = p.dv + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
-        if (p.group == 1) {
+        if (p.group == 1 && !p.accumulate) {
           *dkp = dkacc[db][j] * p.scale;
           *dvp = dvacc[db][j];
+        } else if (p.group == 1) {
+          *dkp += dkacc[db][j] * p.scale;
+          *dvp += dvacc[db][j];
         } else {
           unsafeAtomicAdd(dkp, dkacc[db][j] * p.scale);
           unsafeAtomicAdd(dvp, dvacc[db][j]);

@@ -349,17 +349,23 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32
   return hip_status(rba::launch_bwd_preprocess(p, (hipStream_t)stream), "backward preprocess");
 }
 
-int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
-                 int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse, const float* delta,
-                 float* dq_acc, float* dk_step, float* dv_step, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of rba_bwd_step (dK / dV overwritten) and rba_bwd_step_acc
+// (dK / dV added into accumulators).
+int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
+             int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse, const float* delta,
+             float* dq_acc, float* dk, float* dv, bool accumulate, void* stream) {
   g_err.clear();
   StepPlan plan;
   int rc = prepare_step(a, sq, q_segs, sk, kv_segs, true, plan);
   if (rc) return rc;
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(d_o, "d_o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(delta, "delta")) ||
-      (rc = check_ptr(dq_acc, "dq_acc")) || (rc = check_ptr(dk_step, "dk_step")) ||
-      (rc = check_ptr(dv_step, "dv_step")))
+      (rc = check_ptr(dq_acc, "dq_acc")) || (rc = check_ptr(dk, accumulate ? "dk_acc" : "dk_step")) ||
+      (rc = check_ptr(dv, accumulate ? "dv_acc" : "dv_step")))
     return rc;
   if ((int64_t)sq * a->hq * a->d * 2 >= ((int64_t)1 << 32))
     return fail(RBA_ERR_UNSUPPORTED, "backward step: q and d_o must each be smaller than 4 GiB");
@@ -369,7 +375,8 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
   if ((rc = check_device())) return rc;
   rba::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.d_o = d_o; p.lse = lse; p.delta = delta;
-  p.dk = dk_step; p.dv = dv_step;
+  p.dk = dk; p.dv = dv;
+  p.accumulate = accumulate ? 1 : 0;
   p.sq = (int32_t)sq; p.sk = (int32_t)sk; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
@@ -383,9 +390,9 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
   const int64_t n_wg = (int64_t)p.n_key_tiles * a->hq;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
-  if (p.group > 1) {
+  if (p.group > 1 && !accumulate) {
     // the group's workgroups add their partial dK / dV into zeroed outputs
-    hipError_t e = rba::launch_zero_f32(dk_step, dv_step, sk * a->hkv * a->d, (hipStream_t)stream);
+    hipError_t e = rba::launch_zero_f32(dk, dv, sk * a->hkv * a->d, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "backward zero fill");
   }
   hipError_t e = rba::launch_bwd_dkdv(p, a->d, (hipStream_t)stream);
@@ -395,6 +402,22 @@ int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q
   if ((rc = fill_query_tiling(a, sq, sk, plan, 32, dp.f))) return rc;
   dp.d_o = d_o; dp.lse = lse; dp.delta = delta; dp.dq = dq_acc; dp.scale = a->scale;
   return hip_status(rba::launch_bwd_dq(dp, a->d, (hipStream_t)stream), "backward step (dQ)");
+}
+
+}  // namespace
+
+extern "C" {
+
+int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
+                 int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse, const float* delta,
+                 float* dq_acc, float* dk_step, float* dv_step, void* stream) {
+  return bwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, d_o, lse, delta, dq_acc, dk_step, dv_step, false, stream);
+}
+
+int rba_bwd_step_acc(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k,
+                     const void* v, int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse,
+                     const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
+  return bwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, d_o, lse, delta, dq_acc, dk_acc, dv_acc, true, stream);
 }
 
 }  // extern "C"

@@ -48,8 +48,9 @@ struct BwdParams {
   const void* d_o;
   const float* lse;    // [hq, sq] final log-sum-exp (natural log)
   const float* delta;  // [hq, sq]
-  float* dk;           // [sk, hkv, d] overwritten
-  float* dv;           // [sk, hkv, d] overwritten
+  float* dk;           // [sk, hkv, d]: overwritten, or added into (accumulate)
+  float* dv;           // [sk, hkv, d]
+  int32_t accumulate;  // 1: dk / dv are accumulators (+=); 0: zero-filled outputs
   int32_t sq, sk, hq, hkv, group;
   float scale;
   float scale_log2;

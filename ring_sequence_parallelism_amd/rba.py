@@ -26,7 +26,7 @@ RBA_MAX_SEGS = 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
-EXPORTS = ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step",
+EXPORTS = ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
            "rba_plan_step", "rba_last_error", "rba_version")
 
 
@@ -91,8 +91,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rba_merge.argtypes = [I64, I32, I32, P, P, P, P, P, I32, P]
     lib.rba_bwd_preprocess.argtypes = [I64, I32, I32, I32, I32, P, P, P, P]
     lib.rba_bwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
+    lib.rba_bwd_step_acc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
-    for fn in ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_plan_step"):
+    for fn in ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
+               "rba_plan_step"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
     lib.rba_last_error.argtypes = []
@@ -172,6 +174,14 @@ def rba_bwd_step(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, d_o,
         ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
         ctypes.byref(kv_segs), _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_step),
         _ptr(dv_step), _stream(stream)))
+
+
+def rba_bwd_step_acc(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, d_o, lse, delta,
+                     dq_acc, dk_acc, dv_acc, stream=None) -> int:
+    return _check("rba_bwd_step_acc", load().rba_bwd_step_acc(
+        ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
+        ctypes.byref(kv_segs), _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
+        _ptr(dv_acc), _stream(stream)))
 
 
 def rba_plan_step(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs: rba_segs) -> Tuple[int, int]:

@@ -14,7 +14,7 @@ Device memory comes from torch; every arithmetic step runs in librba.so.
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 import torch
@@ -151,31 +151,38 @@ class RingReplay:
 
     # -- backward ----------------------------------------------------------
     def backward(self, o_saved: Optional[torch.Tensor] = None, lse_saved: Optional[torch.Tensor] = None,
-                 stream=None, on_step=None):
-        """dq (fp32, accumulated over steps) and per-step dk / dv by source rank.
+                 stream=None, on_step=None, dk_acc=None, dv_acc=None):
+        """dq (fp32, accumulated over steps) and per-step dk / dv by step key.
 
         Uses the forward's merged output (the fp32 accumulator by default) and
         merged LSE.  Steps the host proves empty leave their dk / dv zero.
+        With ``dk_acc`` / ``dv_acc`` (dicts by step key of [sk, hkv, d] fp32
+        tensors, the accumulators that travel with each KV chunk) the steps
+        add into those with rba_bwd_step_acc instead, and those are returned.
         """
         assert self.with_grad
         o_saved = self.o_acc if o_saved is None else o_saved
         lse_saved = self.lse_acc if lse_saved is None else lse_saved
+        acc = dk_acc is not None
         if on_step:
             on_step("prep", -1)
         rba.rba_bwd_preprocess(o_saved, self.d_o, self.delta, stream)
         self.dq.zero_()
         for i, s in enumerate(self.steps):
             if s.status != rba.RBA_OK:
-                self.dk[s.src].zero_()
-                self.dv[s.src].zero_()
+                if not acc:
+                    self.dk[s.src].zero_()
+                    self.dv[s.src].zero_()
                 continue
             if on_step:
                 on_step("bwd", i)
-            st = rba.rba_bwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
-                                  self.kv_segs[s.src], self.d_o, lse_saved, self.delta,
-                                  self.dq, self.dk[s.src], self.dv[s.src], stream)
+            step = rba.rba_bwd_step_acc if acc else rba.rba_bwd_step
+            dk = dk_acc[s.src] if acc else self.dk[s.src]
+            dv = dv_acc[s.src] if acc else self.dv[s.src]
+            st = step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src], self.kv_segs[s.src],
+                      self.d_o, lse_saved, self.delta, self.dq, dk, dv, stream)
             assert st == rba.RBA_OK
-        return self.dq, self.dk, self.dv
+        return (self.dq, dk_acc, dv_acc) if acc else (self.dq, self.dk, self.dv)
 
 
 class TaspReplay(RingReplay):
@@ -214,3 +221,25 @@ class TaspReplay(RingReplay):
             self.kv_segs[it] = rba.make_segs(self._tasp_segs[it])
         del chunk_k, chunk_v
         return list(range(w.n_ranks))
+
+
+def full_ring_backward(w: W.Workload, device="cuda", stream=None):
+    """The backward of every rank's ring on one GPU, KV-side gradients summed
+    at their owners: returns dq per rank and dk, dv per chunk (fp32), i.e. the
+    gradients of sum dO * O over the whole sequence.  Each rank's replay adds
+    into the accumulators of the chunks it meets (rba_bwd_step_acc), as the
+    accumulators travelling with the KV chunks would in a real ring."""
+    dk_acc: Dict[int, torch.Tensor] = {}
+    dv_acc: Dict[int, torch.Tensor] = {}
+    dq = {}
+    for r in range(w.n_ranks):
+        rr = RingReplay(w, r, device, with_grad=True)
+        if not dk_acc:
+            for j in range(w.n_ranks):
+                dk_acc[j] = torch.zeros((w.chunk_len, w.hkv, w.d), dtype=torch.float32, device=rr.device)
+                dv_acc[j] = torch.zeros_like(dk_acc[j])
+        rr.forward(stream)
+        d, _, _ = rr.backward(stream=stream, dk_acc=dk_acc, dv_acc=dv_acc)
+        dq[r] = d.clone()
+        del rr
+    return dq, dk_acc, dv_acc

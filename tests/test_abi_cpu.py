@@ -116,12 +116,30 @@ def test_merge_and_preprocess_validation():
     assert lib.rba_bwd_preprocess(8, 2, 64, 0, 5, FAKE, FAKE, FAKE, None) == rba.RBA_ERR_INVALID
 
 
-def test_bwd_rejects_f32():
+@pytest.mark.parametrize("fn", ["rba_bwd_step", "rba_bwd_step_acc"])
+def test_bwd_rejects_f32(fn):
     lib = rba.load()
     a = _attn(dtype=rba.RBA_F32)
-    rc = lib.rba_bwd_step(ctypes.byref(a), FAKE, 64, ctypes.byref(SEG64), FAKE, FAKE, 64,
+    rc = getattr(lib, fn)(ctypes.byref(a), FAKE, 64, ctypes.byref(SEG64), FAKE, FAKE, 64,
                           ctypes.byref(SEG64), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == rba.RBA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["rba_bwd_step", "rba_bwd_step_acc"])
+def test_bwd_null_and_empty(fn):
+    lib = rba.load()
+    a = _attn()
+    f = getattr(lib, fn)
+    args = [ctypes.byref(a), FAKE, 64, ctypes.byref(SEG64), FAKE, FAKE, 64, ctypes.byref(SEG64),
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(args)
+    bad[12] = None                          # dk
+    assert f(*bad) == rba.RBA_ERR_INVALID
+    assert "dk" in rba.rba_last_error()
+    # keys after every query: nothing is launched
+    empty = list(args)
+    empty[7] = ctypes.byref(rba.make_segs([(64, 64)]))
+    assert f(*empty) == rba.RBA_STEP_EMPTY
 
 
 # ---------------------------------------------------------------------------

@@ -180,3 +180,69 @@ def test_replay_c5_full_sampled():
                     got_v[t] = dv[j][where[int(key)], g]
         assert_close(got_k, wdk[:, g], "bf16", f"dk group {g}")
         assert_close(got_v, wdv[:, g], "bf16", f"dv group {g}")
+
+
+# ---------------------------------------------------------------------------
+# KV-side accumulation (rba_bwd_step_acc)
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2)])
+def test_step_acc_adds_into_accumulators(hq, hkv):
+    """rba_bwd_step_acc adds exactly what rba_bwd_step writes (bit for bit with
+    one query head per KV head, where each element is added once)."""
+    sq, sk, d = 200, 333, 128
+    _say("bwd step acc", hq, hkv)
+    rng = np.random.default_rng(hq * 10 + hkv)
+    qb, _ = _bf16(rng, (sq, hq, d))
+    kb, _ = _bf16(rng, (sk, hkv, d))
+    vb, _ = _bf16(rng, (sk, hkv, d))
+    dob, _ = _bf16(rng, (sq, hq, d))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    a = rba.attn_params(hq, hkv, d, scale, rba.RBA_BF16, rba.RBA_MASK_CAUSAL)
+    q, k, v, dO = (to_device(x, "bf16", DEV) for x in (qb, kb, vb, dob))
+    qs, ks = rba.make_segs([(100, sq)]), rba.make_segs([(0, sk)])
+    o = torch.empty((sq, hq, d), device=DEV)
+    lse = torch.empty((hq, sq), device=DEV)
+    assert rba.rba_fwd_step(a, q, qs, k, v, ks, o, lse) == rba.RBA_OK
+    delta = torch.empty((hq, sq), device=DEV)
+    rba.rba_bwd_preprocess(o, dO, delta)
+    dq1 = torch.zeros((sq, hq, d), device=DEV)
+    dk1 = torch.empty((sk, hkv, d), device=DEV)
+    dv1 = torch.empty((sk, hkv, d), device=DEV)
+    assert rba.rba_bwd_step(a, q, qs, k, v, ks, dO, lse, delta, dq1, dk1, dv1) == rba.RBA_OK
+    base_k = torch.from_numpy(rng.standard_normal((sk, hkv, d)).astype(np.float32)).to(DEV)
+    base_v = torch.from_numpy(rng.standard_normal((sk, hkv, d)).astype(np.float32)).to(DEV)
+    dq2 = torch.zeros((sq, hq, d), device=DEV)
+    dk2, dv2 = base_k.clone(), base_v.clone()
+    assert rba.rba_bwd_step_acc(a, q, qs, k, v, ks, dO, lse, delta, dq2, dk2, dv2) == rba.RBA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)
+    if hq == hkv:
+        assert torch.equal(dk2, base_k + dk1) and torch.equal(dv2, base_v + dv1)
+    else:
+        assert torch.allclose(dk2, base_k + dk1, rtol=1e-5, atol=1e-5)
+        assert torch.allclose(dv2, base_v + dv1, rtol=1e-5, atol=1e-5)
+    # an empty step leaves the accumulators untouched
+    before = dk2.clone()
+    st = rba.rba_bwd_step_acc(a, q, qs, k, v, rba.make_segs([(10_000, sk)]), dO, lse, delta, dq2, dk2, dv2)
+    torch.cuda.synchronize()
+    assert st == rba.RBA_STEP_EMPTY and torch.equal(dk2, before)
+
+
+def test_full_ring_backward_scaled():
+    """Every rank's ring on one GPU with owner-side dK / dV accumulation gives
+    the gradients of the whole sequence."""
+    from ring_sequence_parallelism_amd.ring import full_ring_backward
+    w = W.scaled_workload(W.WORKLOADS["c5"], 4096, hq=8, hkv=2)
+    _say("full ring backward", w.name)
+    dq, dk, dv = full_ring_backward(w, DEV)
+    torch.cuda.synchronize()
+    q64 = W.to_f64(W.gen_pieces(w, W.T_Q, range(w.n_pieces)), w.dtype)
+    do64 = W.to_f64(W.gen_pieces(w, W.T_DO, range(w.n_pieces)), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    pos = np.arange(w.seq)
+    wdq, wdk, wdv, *_ = oracle.attention_backward(q64, k64, v64, do64, pos, pos, w.mask, w.scale)
+    for j in range(w.n_ranks):
+        p = chunk_positions(w, j)
+        assert_close(dq[j].cpu().numpy(), wdq[p], "bf16", f"dq rank {j}")
+        assert_close(dk[j].cpu().numpy(), wdk[p], "bf16", f"dk chunk {j}")
+        assert_close(dv[j].cpu().numpy(), wdv[p], "bf16", f"dv chunk {j}")
