@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librba.so")
 
-SOURCES = ["rba_host.cpp", "rba_fwd.hip", "rba_merge.hip", "rba_bwd.hip", "rba_bwd_dq.hip"]
+SOURCES = ["rba_host.cpp", "rba_fwd.hip", "rba_merge.hip", "rba_bwd.hip"]
 ARCH = "gfx950"
 
 

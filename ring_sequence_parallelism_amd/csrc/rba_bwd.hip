@@ -34,6 +34,7 @@
 //     loads and barrier; issue block i + 1's loads; compute block i.
 #include <type_traits>
 
+#include "rba_bwd_dq.h"
 #include "rba_device.h"
 
 namespace rba {
@@ -99,22 +100,29 @@ __device__ __forceinline__ int classify_keys(int mask, PosRange k, bool k_bad, i
   return (full && !k_bad) ? kFull : kPartial;
 }
 
+// LDS bytes of the dK / dV body: the K tile, double-buffered Q / dO tiles
+// and LSE / delta rows.
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
+constexpr int dkdv_lds_bytes() { return kBK * D * 2 + 2 * 2 * kBQ * D * 2 + 2 * 2 * 64 * 4; }
+
+// One workgroup (4 waves, number `wg` of p.n_wg) of the dK / dV pass, with
+// `smem` the workgroup's LDS (dkdv_lds_bytes<D>() bytes, 16-byte aligned).
+template <int D>
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* smem) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
   constexpr int QT = kBQ * RB;               // bytes of a Q or dO block tile
   constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
   // K tile (once), double-buffered Q / dO tiles and LSE / delta rows (loaded
   // straight from HBM into LDS).
-  __shared__ __attribute__((aligned(16))) char k_lds[kBK * RB];
-  __shared__ __attribute__((aligned(16))) char qd_lds[2][2][QT];          // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][64];         // [buffer][lse, delta][row]
+  char* k_lds = smem;
+  char (*qd_lds)[2][QT] = reinterpret_cast<char (*)[2][QT]>(smem + kBK * RB);          // [buffer][Q, dO]
+  float (*ld_lds)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + kBK * RB + 4 * QT);   // [buffer][lse, delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int col = lane & 31, half = lane >> 5;
-  const int logical = xcd_remap(blockIdx.x, p.n_wg);
+  const int logical = xcd_remap(wg, p.n_wg);
   const int g = logical / (p.n_key_tiles * p.group);
   const int kt = (logical / p.group) % p.n_key_tiles;
   const int h = g * p.group + logical % p.group;   // the query head of this workgroup
@@ -368,12 +376,27 @@ int bwd_keys_per_wg(int d) {
   return kBK;
 }
 
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s) {
-  dim3 grid(p.n_wg), block(kBwdThreads);
+// The backward step in one launch: workgroups [0, p.n_wg) run the dK / dV
+// pass (heaviest key tiles first), the following dp.f.n_wg the dQ pass, which
+// fills the CUs as the dK / dV tail drains.  The two passes share no output
+// and read the same inputs.  LDS is one buffer sized for the larger body.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_kernel(BwdParams p, DqParams dp) {
+  constexpr int SMEM = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  const int b = blockIdx.x;
+  if (b < p.n_wg)
+    bwd_dkdv_body<D>(p, b, smem);
+  else
+    bwd_dq_body<D>(dp, b - p.n_wg, smem);
+}
+
+hipError_t launch_bwd(const BwdParams& p, const DqParams& dp, int d, hipStream_t s) {
+  dim3 grid(p.n_wg + dp.f.n_wg), block(kBwdThreads);
   if (d == 128)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_kernel<128>, grid, block, 0, s, p, dp);
   else if (d == 64)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_kernel<64>, grid, block, 0, s, p, dp);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -17,24 +17,35 @@
 //                      to bf16 in the key order of the accumulator rows)
 // Each (row, head) of dq_acc belongs to one wave: the kernel adds its
 // contribution with one read-modify-write at the end, no atomics.
+//
+// This is a device-side body: the backward step runs it in the same launch
+// as the dK / dV pass (rba_bwd.hip).
+#pragma once
+
 #include <type_traits>
 
 #include "rba_qtile.h"
 
 namespace rba {
 
+// LDS bytes of the dQ body: double-buffered K and V tiles.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams dp) {
+constexpr int dq_lds_bytes() { return 2 * 2 * kBN * D * 2; }
+
+// One workgroup (4 waves, number `block` of dp.f.n_wg) of the dQ pass, with
+// `smem` the workgroup's LDS (dq_lds_bytes<D>() bytes, 16-byte aligned).
+template <int D>
+__device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char* smem) {
   const FwdParams& p = dp.f;
   constexpr int CPR = D / 8;
   constexpr int RB = D * 2;
   constexpr int TILE = kBN * RB;
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];   // [buffer][K, V]
+  char (*lds)[2][TILE] = reinterpret_cast<char (*)[2][TILE]>(smem);   // [buffer][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<32>(p, wave);
+  const WaveTask t = make_task<32>(p, wave, block);
   const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
 
   // Q^T and dO^T as B operands: lane holds query `col`, d = 16*ks + 8*half + 0..7.
@@ -145,17 +156,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DqParams dp) {
         *q4 = *q4 + add * dp.scale;
       }
   }
-}
-
-hipError_t launch_bwd_dq(const DqParams& p, int d, hipStream_t s) {
-  dim3 grid(p.f.n_wg), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, block, 0, s, p);
-  else if (d == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, block, 0, s, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace rba

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<QR>(p, wave);
+  const WaveTask t = make_task<QR>(p, wave, blockIdx.x);
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<QR>(p, __builtin_amdgcn_readfirstlane(tid >> 6));
+  const WaveTask t = make_task<QR>(p, __builtin_amdgcn_readfirstlane(tid >> 6), blockIdx.x);
   const float* kbase = static_cast<const float*>(p.k);
   const float* vbase = static_cast<const float*>(p.v);
 

@@ -395,13 +395,12 @@ int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
     hipError_t e = rba::launch_zero_f32(dk, dv, sk * a->hkv * a->d, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "backward zero fill");
   }
-  hipError_t e = rba::launch_bwd_dkdv(p, a->d, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "backward step (dK, dV)");
   rba::DqParams dp{};
   dp.f.q = q; dp.f.k = k; dp.f.v = v;
   if ((rc = fill_query_tiling(a, sq, sk, plan, 32, dp.f))) return rc;
   dp.d_o = d_o; dp.lse = lse; dp.delta = delta; dp.dq = dq_acc; dp.scale = a->scale;
-  return hip_status(rba::launch_bwd_dq(dp, a->d, (hipStream_t)stream), "backward step (dQ)");
+  if ((int64_t)p.n_wg + dp.f.n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
+  return hip_status(rba::launch_bwd(p, dp, a->d, (hipStream_t)stream), "backward step");
 }
 
 }  // namespace

@@ -98,8 +98,8 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s);
-hipError_t launch_bwd_dq(const DqParams& p, int d, hipStream_t s);
+// The backward step's dK / dV and dQ passes, in one launch.
+hipError_t launch_bwd(const BwdParams& p, const DqParams& dp, int d, hipStream_t s);
 hipError_t launch_zero_f32(float* a, float* b, int64_t n, hipStream_t s);
 
 // Rows of the forward workgroup tile per wave (32 * fwd_row_blocks).

@@ -24,8 +24,8 @@ struct WaveTask {
 };
 
 template <int QR>
-__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave) {
-  const int logical = xcd_remap(blockIdx.x, p.n_wg);
+__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int block) {
+  const int logical = xcd_remap(block, p.n_wg);
   const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
   const int rg = logical % p.n_row_groups;
   WaveTask t;
