@@ -121,6 +121,26 @@ int rba_fwd_step(const rba_attn* a,
                  float* o_part, float* lse_part, void* stream);
 
 /*
+ * rba_fwd_step_acc — rba_fwd_step whose partial is merged, in the same
+ * launch, into a running result: with the step's partial (O_s, LSE_s),
+ *   L = ln(e^{lse_acc} + e^{LSE_s}),
+ *   o_acc = e^{lse_acc - L} o_acc + e^{LSE_s - L} O_s,   lse_acc = L
+ * (the merge of rba_merge, the same arithmetic), and when o_final is
+ * non-NULL the merged O is also written to it in final_dtype (RBA_BF16 or
+ * RBA_F32) — the last step of a replay.  o_acc [sq, hq, d] and lse_acc
+ * [hq, sq] fp32 are in/out and must already hold a result (the first step
+ * of a ring goes through rba_fwd_step).  This saves the partial's round
+ * trip through HBM and the merge launch.  Same inputs, limits and errors as
+ * rba_fwd_step; o_final must not alias o_acc.  On RBA_STEP_EMPTY nothing is
+ * launched: o_acc / lse_acc are unchanged and o_final is NOT written (finish
+ * with rba_merge and no partial).
+ */
+int rba_fwd_step_acc(const rba_attn* a,
+                     const void* q, int64_t sq, const rba_segs* q_segs,
+                     const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                     float* o_acc, float* lse_acc, void* o_final, int32_t final_dtype, void* stream);
+
+/*
  * rba_merge — LSE-weighted merge of a step's partial into the running result.
  *   L = ln(e^{lse_acc} + e^{lse_part}),
  *   o_acc = e^{lse_acc - L} o_acc + e^{lse_part - L} o_part,  lse_acc = L.

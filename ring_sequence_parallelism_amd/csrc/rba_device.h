@@ -100,6 +100,29 @@ __device__ __forceinline__ bool visible(int mask, int32_t kp, int32_t qp, int32_
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Weights of the LSE-weighted merge of two partial results over disjoint key
+// sets (blockwise exact attention, FlashAttention in the TASP citation map):
+// with L = ln(e^la + e^lb), O = wa Oa + wb Ob for wa = e^(la - L),
+// wb = e^(lb - L).  A side with LSE = -inf has weight 0; two such sides give
+// weights 0 and L = -inf.  Shared by the merge kernel and the forward step's
+// merging epilogue, so both round alike.
+struct MergeWeights {
+  float wa, wb, L;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float la, float lb) {
+  const float mx = fmaxf(la, lb);
+  MergeWeights w{0.f, 0.f, -INFINITY};
+  if (mx != -INFINITY) {
+    const float a = __expf(la - mx), b = __expf(lb - mx);
+    const float s = a + b;
+    w.L = mx + __logf(s);
+    const float inv = 1.f / s;
+    w.wa = a * inv;
+    w.wb = b * inv;
+  }
+  return w;
+}
+
 // Both halves of a wave: lane l gets {v[l % 32], v[l % 32 + 32]}.
 __device__ __forceinline__ float half_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

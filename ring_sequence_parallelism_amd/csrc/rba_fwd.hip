@@ -201,22 +201,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const float l = half_sum(l_run[qb]);
-    const int row = t.row0 + qb * 32 + col;
     const bool has = l > 0.f;
     const float inv = has ? 1.f / l : 0.f;
     const float lse = has ? m_run[qb] * kLn2 + __logf(l) : -INFINITY;
-    if (row < p.sq) {
-      if (half == 0) p.lse[(size_t)t.h * p.sq + row] = lse;
-      float* dst = p.o + ((size_t)row * p.hq + t.h) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          f32x4 val = {oacc[qb][db][4 * jj] * inv, oacc[qb][db][4 * jj + 1] * inv,
-                       oacc[qb][db][4 * jj + 2] * inv, oacc[qb][db][4 * jj + 3] * inv};
-          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
-        }
-    }
+    write_step_output<D>(p, t.row0 + qb * 32 + col, t.h, half, oacc[qb], inv, lse);
   }
 }
 
@@ -351,18 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
   const float lse = has ? m_run * kLn2 + __logf(l) : -INFINITY;
-  if (row_ok) {
-    if (half == 0) p.lse[(size_t)t.h * p.sq + row] = lse;
-    float* dst = p.o + ((size_t)row * p.hq + t.h) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4 val = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
-                     oacc[db][4 * jj + 3] * inv};
-        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
-      }
-  }
+  write_step_output<D>(p, row, t.h, half, oacc, inv, lse);
 }
 
 // ---------------------------------------------------------------------------

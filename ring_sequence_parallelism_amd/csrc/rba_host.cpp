@@ -260,6 +260,40 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   return RBA_OK;
 }
 
+// Shared body of rba_fwd_step (partial written to o / lse) and
+// rba_fwd_step_acc (partial merged into the running o / lse).
+int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
+             int64_t sk, const rba_segs* kv_segs, float* o, float* lse, bool accumulate, void* o_final,
+             int32_t final_dtype, void* stream) {
+  g_err.clear();
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, accumulate ? "o_acc" : "o_part")) || (rc = check_ptr(lse, accumulate ? "lse_acc" : "lse_part")))
+    return rc;
+  if (o_final) {
+    if (final_dtype != RBA_BF16 && final_dtype != RBA_F32)
+      return fail(RBA_ERR_INVALID, "unknown final dtype %d", final_dtype);
+    if ((rc = check_ptr(o_final, "o_final"))) return rc;
+    if (o_final == (void*)o) return fail(RBA_ERR_INVALID, "o_final aliases o_acc");
+  }
+  const bool bf16 = a->dtype == RBA_BF16;
+  if (bf16 && sk * a->hkv * a->d * 2 >= ((int64_t)1 << 32))
+    return fail(RBA_ERR_UNSUPPORTED, "forward step: k and v must each be smaller than 4 GiB");
+  if (plan.empty) return RBA_STEP_EMPTY;
+  if ((rc = check_device())) return rc;
+
+  rba::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.accumulate = accumulate ? 1 : 0;
+  p.o_final = o_final;
+  p.final_bf16 = final_dtype == RBA_BF16;
+  if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, bf16), p))) return rc;
+  hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
+  return hip_status(e, "forward step");
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,24 +317,13 @@ int rba_plan_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t
 
 int rba_fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
                  int64_t sk, const rba_segs* kv_segs, float* o_part, float* lse_part, void* stream) {
-  g_err.clear();
-  StepPlan plan;
-  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
-  if (rc) return rc;
-  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
-      (rc = check_ptr(o_part, "o_part")) || (rc = check_ptr(lse_part, "lse_part")))
-    return rc;
-  const bool bf16 = a->dtype == RBA_BF16;
-  if (bf16 && sk * a->hkv * a->d * 2 >= ((int64_t)1 << 32))
-    return fail(RBA_ERR_UNSUPPORTED, "forward step: k and v must each be smaller than 4 GiB");
-  if (plan.empty) return RBA_STEP_EMPTY;
-  if ((rc = check_device())) return rc;
+  return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o_part, lse_part, false, nullptr, 0, stream);
+}
 
-  rba::FwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = o_part; p.lse = lse_part;
-  if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, bf16), p))) return rc;
-  hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
-  return hip_status(e, "forward step");
+int rba_fwd_step_acc(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k,
+                     const void* v, int64_t sk, const rba_segs* kv_segs, float* o_acc, float* lse_acc,
+                     void* o_final, int32_t final_dtype, void* stream) {
+  return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o_acc, lse_acc, true, o_final, final_dtype, stream);
 }
 
 int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, const float* o_part,

@@ -23,8 +23,11 @@ struct FwdParams {
   const void* q;
   const void* k;
   const void* v;
-  float* o;            // [sq, hq, d] fp32 partial output
-  float* lse;          // [hq, sq] fp32 partial log-sum-exp
+  float* o;            // [sq, hq, d] fp32 partial output, or the running output (accumulate)
+  float* lse;          // [hq, sq] fp32 partial log-sum-exp, or the running one
+  int32_t accumulate;  // 1: merge the step's partial into (o, lse) in place
+  void* o_final;       // accumulate only, may be null: also write the merged output
+  int32_t final_bf16;  // 1: o_final is bf16, 0: fp32
   int32_t sq, sk, hq, hkv, group;
   float scale_log2;    // softmax scale * log2(e): scores are exponentiated in base 2
   int32_t mask;        // RBA_MASK_*

@@ -28,22 +28,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     const size_t oi = (size_t)pair * p.d + 4 * c4;
     f32x4 o = *reinterpret_cast<const f32x4*>(p.o_acc + oi);
     if (p.o_part) {
-      const float la = p.lse_acc[li], lb = p.lse_part[li];
-      const float mx = fmaxf(la, lb);
-      float wa = 0.f, wb = 0.f, L = -INFINITY;
-      if (mx != -INFINITY) {
-        wa = __expf(la - mx);
-        wb = __expf(lb - mx);
-        const float s = wa + wb;
-        L = mx + __logf(s);
-        const float inv = 1.f / s;
-        wa *= inv;
-        wb *= inv;
-      }
+      const MergeWeights w = merge_weights(p.lse_acc[li], p.lse_part[li]);
       const f32x4 ob = *reinterpret_cast<const f32x4*>(p.o_part + oi);
-      o = wa * o + wb * ob;
+      o = w.wa * o + w.wb * ob;
       *reinterpret_cast<f32x4*>(p.o_acc + oi) = o;
-      if (c4 == 0) p.lse_acc[li] = L;
+      if (c4 == 0) p.lse_acc[li] = w.L;
     }
     if (p.o_final) {
       if (p.final_bf16) {

@@ -191,4 +191,58 @@ __device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const 
   }
 }
 
+// Writes one lane's share of a query row's step result: O = oacc / l (this
+// lane's 16 elements of each 32-column block db: d = 32 db + 8 (j / 4) +
+// 4 half + j % 4, four consecutive d per vector) and the row's LSE.  Rows
+// with no allowed key have inv = 0 and lse = -inf.  In accumulate mode the
+// result is merged into the running (O, LSE) instead (merge_weights), and
+// the merged O is also written to o_final when one is given.  Both lanes of
+// a row read the running LSE before either writes it (the write depends on
+// the read's value).
+template <int D>
+__device__ __forceinline__ void write_step_output(const FwdParams& p, int row, int h, int half,
+                                                  const f32x16 (&oacc)[D / 32], float inv, float lse) {
+  if (row >= p.sq) return;
+  const size_t li = (size_t)h * p.sq + row;
+  const size_t oi = ((size_t)row * p.hq + h) * D;
+  float* dst = p.o + oi;
+  if (!p.accumulate) {
+    if (half == 0) p.lse[li] = lse;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 val = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                           oacc[db][4 * jj + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
+      }
+    return;
+  }
+  f32x4 old[D / 32][4];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) old[db][jj] = *reinterpret_cast<const f32x4*>(dst + db * 32 + 8 * jj + 4 * half);
+  const MergeWeights w = merge_weights(p.lse[li], lse);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 part = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                          oacc[db][4 * jj + 3] * inv};
+      const f32x4 o = w.wa * old[db][jj] + w.wb * part;
+      const int c = db * 32 + 8 * jj + 4 * half;
+      *reinterpret_cast<f32x4*>(dst + c) = o;
+      if (p.o_final) {
+        if (p.final_bf16) {
+          const u32x2 b = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi + c) = b;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi + c) = o;
+        }
+      }
+    }
+  if (half == 0) p.lse[li] = w.L;
+}
+
 }  // namespace rba

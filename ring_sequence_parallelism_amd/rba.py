@@ -26,7 +26,7 @@ RBA_MAX_SEGS = 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
-EXPORTS = ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
+EXPORTS = ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
            "rba_plan_step", "rba_last_error", "rba_version")
 
 
@@ -88,12 +88,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     A, S = ctypes.POINTER(rba_attn), ctypes.POINTER(rba_segs)
     lib.rba_fwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P]
+    lib.rba_fwd_step_acc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, I32, P]
     lib.rba_merge.argtypes = [I64, I32, I32, P, P, P, P, P, I32, P]
     lib.rba_bwd_preprocess.argtypes = [I64, I32, I32, I32, I32, P, P, P, P]
     lib.rba_bwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_bwd_step_acc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
-    for fn in ("rba_fwd_step", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
+    for fn in ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
                "rba_plan_step"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
@@ -144,6 +145,13 @@ def rba_fwd_step(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs,
     return _check("rba_fwd_step", load().rba_fwd_step(
         ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
         ctypes.byref(kv_segs), _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def rba_fwd_step_acc(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, o_acc, lse_acc,
+                     o_final=None, final_dtype: int = RBA_BF16, stream=None) -> int:
+    return _check("rba_fwd_step_acc", load().rba_fwd_step_acc(
+        ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
+        ctypes.byref(kv_segs), _ptr(o_acc), _ptr(lse_acc), _ptr(o_final), final_dtype, _stream(stream)))
 
 
 def rba_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None, final_dtype: int = RBA_BF16,

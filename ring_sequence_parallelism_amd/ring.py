@@ -120,9 +120,13 @@ class RingReplay:
         return rba.rba_fwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
                                 self.kv_segs[s.src], o, l, stream)
 
-    def forward(self, stream=None, on_step=None) -> torch.Tensor:
+    def forward(self, stream=None, on_step=None, fused_merge: bool = True) -> torch.Tensor:
         """Replay all steps; returns o_final (merged output in the input dtype).
 
+        The first live step writes the running result (o_acc, lse_acc); each
+        later one is merged into it by rba_fwd_step_acc in the same launch
+        (``fused_merge``, the last one also writing o_final), or, with
+        ``fused_merge=False``, goes through o_part / lse_part and rba_merge.
         ``on_step(kind, i)`` is called before each launch ("fwd" / "merge") so
         a caller can bracket launches with events.
         """
@@ -135,12 +139,18 @@ class RingReplay:
             return self.o_final
         for n_done, i in enumerate(live):
             first = n_done == 0
+            last = n_done == len(live) - 1
             if on_step:
                 on_step("fwd", i)
-            st = self.fwd_step(i, into_acc=first, stream=stream)
+            if first or not fused_merge:
+                st = self.fwd_step(i, into_acc=first, stream=stream)
+            else:
+                s = self.steps[i]
+                st = rba.rba_fwd_step_acc(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                          self.kv_segs[s.src], self.o_acc, self.lse_acc,
+                                          self.o_final if last else None, final_dtype, stream)
             assert st == rba.RBA_OK, "host plan and step status disagree"
-            if not first:
-                last = n_done == len(live) - 1
+            if not first and not fused_merge:
                 if on_step:
                     on_step("merge", i)
                 rba.rba_merge(self.o_acc, self.lse_acc, self.o_part, self.lse_part,

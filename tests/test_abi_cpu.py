@@ -216,3 +216,26 @@ def test_plan_packed_docs_total():
     lens = np.diff(cu.astype(np.int64))
     assert tot == int((lens * (lens + 1) // 2).sum())
     assert 16 <= nonempty < 256
+
+
+def test_fwd_step_acc_validation():
+    lib = rba.load()
+    a = _attn(mask=rba.RBA_MASK_NONE)
+    f = lib.rba_fwd_step_acc
+    args = [ctypes.byref(a), FAKE, 64, ctypes.byref(SEG64), FAKE, FAKE, 64, ctypes.byref(SEG64),
+            ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), None, rba.RBA_BF16, None]
+    bad = list(args)
+    bad[10], bad[11] = ctypes.c_void_p(0x40000), 9          # final dtype unknown
+    assert f(*bad) == rba.RBA_ERR_INVALID
+    bad = list(args)
+    bad[10] = ctypes.c_void_p(0x20000)                       # o_final aliases o_acc
+    assert f(*bad) == rba.RBA_ERR_INVALID
+    bad = list(args)
+    bad[9] = None                                            # no lse_acc
+    assert f(*bad) == rba.RBA_ERR_INVALID
+    assert "lse_acc" in rba.rba_last_error()
+    ac = _attn()
+    empty = list(args)
+    empty[0] = ctypes.byref(ac)
+    empty[7] = ctypes.byref(rba.make_segs([(64, 64)]))       # keys after every query
+    assert f(*empty) == rba.RBA_STEP_EMPTY

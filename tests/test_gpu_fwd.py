@@ -300,3 +300,75 @@ def test_per_step_partials_c2():
         wo, wl = oracle.attention(q64, k64, v64, qpos, kpos, w.mask, w.scale)
         assert_lse(rr.lse_part.cpu().numpy()[:, rows], wl, f"step {i} lse")
         assert_close(rr.o_part.cpu().numpy()[rows], wo, "bf16", f"step {i} o")
+
+
+# ---------------------------------------------------------------------------
+# forward step with the merge in its epilogue (rba_fwd_step_acc)
+
+@pytest.mark.parametrize("final", [None, "bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_step_acc_equals_step_plus_merge(final, d):
+    """rba_fwd_step_acc gives what rba_fwd_step followed by rba_merge gives,
+    including accumulator rows with LSE = -inf and step rows without keys."""
+    _say("fwd step acc", d, final)
+    rng = np.random.default_rng(40 + d)
+    sq, sk, hq, hkv = 150, 200, 4, 2
+    qb, _ = _rand_inputs(rng, sq, hq, d, "bf16")
+    kb, _ = _rand_inputs(rng, sk, hkv, d, "bf16")
+    vb, _ = _rand_inputs(rng, sk, hkv, d, "bf16")
+    q, k, v = (to_device(x, "bf16", DEV) for x in (qb, kb, vb))
+    a = rba.attn_params(hq, hkv, d, float(np.float32(1 / np.sqrt(d))), rba.RBA_BF16, rba.RBA_MASK_CAUSAL)
+    qs, ks = rba.make_segs([(100, sq)]), rba.make_segs([(120, sk)])    # rows 0..19 (positions 100..119) see no key
+    acc0 = torch.from_numpy(rng.standard_normal((sq, hq, d)).astype(np.float32)).to(DEV)
+    lse0 = torch.from_numpy((rng.standard_normal((hq, sq)) * 2).astype(np.float32)).to(DEV)
+    lse0[0, 0:30] = float("-inf")                                       # rows 0..19 empty on both sides
+    acc0[0:30, 0] = 0
+    # reference: partial, then the merge kernel
+    o_part = torch.empty((sq, hq, d), device=DEV)
+    l_part = torch.empty((hq, sq), device=DEV)
+    assert rba.rba_fwd_step(a, q, qs, k, v, ks, o_part, l_part) == rba.RBA_OK
+    o_ref, l_ref = acc0.clone(), lse0.clone()
+    fdt = rba.RBA_BF16 if final != "f32" else rba.RBA_F32
+    tdt = torch.bfloat16 if final != "f32" else torch.float32
+    f_ref = torch.full((sq, hq, d), 7.0, dtype=tdt, device=DEV) if final else None
+    rba.rba_merge(o_ref, l_ref, o_part, l_part, f_ref, fdt)
+    # fused
+    o_acc, l_acc = acc0.clone(), lse0.clone()
+    f_acc = torch.full((sq, hq, d), 7.0, dtype=tdt, device=DEV) if final else None
+    assert rba.rba_fwd_step_acc(a, q, qs, k, v, ks, o_acc, l_acc, f_acc, fdt) == rba.RBA_OK
+    torch.cuda.synchronize()
+    assert torch.allclose(o_acc, o_ref, rtol=2e-6, atol=2e-6)
+    assert torch.equal(torch.isneginf(l_acc), torch.isneginf(l_ref))
+    fin = ~torch.isneginf(l_ref)
+    assert torch.allclose(l_acc[fin], l_ref[fin], rtol=1e-6, atol=1e-6)
+    assert (o_acc[0:20, 0] == 0).all()                    # empty in both: (0, -inf)
+    assert torch.isneginf(l_acc[0, 0:20]).all()
+    assert torch.allclose(o_acc[20:30, 0], o_part[20:30, 0], rtol=1e-6, atol=1e-6)   # empty accumulator
+    if final:
+        assert torch.allclose(f_acc.float(), f_ref.float(), rtol=1e-2 if final == "bf16" else 2e-6, atol=2e-6)
+    # an empty step changes nothing and writes no final output
+    before_o, before_l = o_acc.clone(), l_acc.clone()
+    f2 = torch.full((sq, hq, d), 7.0, dtype=tdt, device=DEV) if final else None
+    st = rba.rba_fwd_step_acc(a, q, qs, k, v, rba.make_segs([(5000, sk)]), o_acc, l_acc, f2, fdt)
+    torch.cuda.synchronize()
+    assert st == rba.RBA_STEP_EMPTY
+    assert torch.equal(o_acc, before_o) and torch.equal(l_acc, before_l)
+    if final:
+        assert (f2.float() == 7.0).all()
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_replay_merge_paths_agree(fused):
+    """The replay through rba_fwd_step_acc and through o_part + rba_merge both
+    match unchunked attention."""
+    w = W.scaled_workload(W.WORKLOADS["c2"], 4096, hq=8, hkv=2)
+    _say("replay merge path", "fused" if fused else "separate")
+    rr = RingReplay(w, 5, DEV)
+    rr.forward(fused_merge=fused)
+    torch.cuda.synchronize()
+    qpos = chunk_positions(w, 5)
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, 5), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    want_o, want_l = oracle.attention(q64, k64, v64, qpos, np.arange(w.seq), w.mask, w.scale)
+    assert_lse(rr.lse_acc.cpu().numpy(), want_l, "lse")
+    assert_close(rr.o_final.float().cpu().numpy(), want_o, "bf16", "o")
