@@ -5,10 +5,11 @@ the all-to-all topology of n accelerators -- the complete directed graph on n
 nodes -- into n - 1 arc-disjoint directed Hamiltonian cycles, and splits the
 ring all-gather of KV chunks into the same number of concurrent ring
 transfers.  The pages give no slicing rule; the reading used here is the
-plainest one: every KV chunk is cut into n - 1 contiguous row slices, slice c
-travels along cycle c, and at each iteration every node forwards to its
-successor on cycle c the slice it received on that cycle one iteration
-earlier (at iteration 1, its own slice c).
+plainest one: every KV chunk is cut into n - 1 contiguous row slices (near
+equal, with boundaries on the 64-row key tile), slice c travels along cycle
+c, and at each iteration every node forwards to its successor on cycle c the
+slice it received on that cycle one iteration earlier (at iteration 1, its
+own slice c).
 
 So at iteration s (1 <= s <= n - 1) rank r holds, for every cycle c, slice c
 of the chunk that started s hops before r on cycle c.  Over the n - 1
@@ -79,16 +80,26 @@ def hamiltonian_decomposition(n: int) -> List[List[int]]:
     return cycles
 
 
-def slice_bounds(rows: int, n_slices: int) -> List[Tuple[int, int]]:
-    """Contiguous row ranges [a, b) cutting `rows` rows into n_slices near-equal
-    slices (the first rows % n_slices slices one row longer)."""
-    base, extra = divmod(rows, n_slices)
-    out, a = [], 0
+def slice_bounds(rows: int, n_slices: int, align: int = 1) -> List[Tuple[int, int]]:
+    """Contiguous row ranges [a, b) cutting `rows` rows into n_slices slices
+    whose boundaries fall on multiples of `align` rows: the ceil(rows / align)
+    units are shared out near-equally (the first ones get one unit more), so
+    slice sizes differ by at most `align` rows; the last slice ends at `rows`.
+    With fewer units than slices the trailing slices are empty."""
+    units = -(-rows // align)
+    base, extra = divmod(units, n_slices)
+    out, u = [], 0
     for c in range(n_slices):
-        b = a + base + (1 if c < extra else 0)
-        out.append((a, b))
-        a = b
+        v = u + base + (1 if c < extra else 0)
+        out.append((min(u * align, rows), min(v * align, rows)))
+        u = v
     return out
+
+
+# Slice boundaries on multiples of the kernels' 64-row key tile, so that no
+# key tile straddles two slices (a straddling tile holds rows of two source
+# chunks and takes the per-element mask path).
+SLICE_ALIGN = 64
 
 
 @dataclasses.dataclass
@@ -124,8 +135,9 @@ class TaspSchedule:
         """The KV slices of iteration `it` (0: the rank's own chunk, whole)."""
         if it == 0:
             return [SliceRef(rank, -1, (0, chunk_len))]
-        bounds = slice_bounds(chunk_len, len(self.cycles))
-        return [SliceRef(self.source(rank, it, c), c, bounds[c]) for c in range(len(self.cycles))]
+        bounds = slice_bounds(chunk_len, len(self.cycles), SLICE_ALIGN)
+        return [SliceRef(self.source(rank, it, c), c, bounds[c]) for c in range(len(self.cycles))
+                if bounds[c][1] > bounds[c][0]]
 
 
 def slice_segments(w: W.Workload, ref: SliceRef) -> List[Tuple[int, int]]:

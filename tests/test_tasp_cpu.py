@@ -65,13 +65,16 @@ def test_every_slice_arrives_once(n):
             assert sorted(srcs) == [x for x in range(n) if x != r]
 
 
-@pytest.mark.parametrize("rows,k", [(4096, 7), (10, 7), (7, 7), (5, 7), (1, 3)])
-def test_slice_bounds_partition(rows, k):
-    b = tasp.slice_bounds(rows, k)
+@pytest.mark.parametrize("align", [1, 64])
+@pytest.mark.parametrize("rows,k", [(4096, 7), (10, 7), (7, 7), (5, 7), (1, 3), (65536, 7), (4096, 15), (700, 7)])
+def test_slice_bounds_partition(rows, k, align):
+    b = tasp.slice_bounds(rows, k, align)
     assert len(b) == k and b[0][0] == 0 and b[-1][1] == rows
     assert all(b[i][1] == b[i + 1][0] for i in range(k - 1))
+    assert all(x % align == 0 for x, _ in b if x < rows)          # boundaries on the alignment
     sizes = [y - x for x, y in b]
-    assert max(sizes) - min(sizes) <= 1
+    full = [z for z in sizes[:-1]] + ([sizes[-1]] if rows % align == 0 else [])
+    assert max(full) - min(full) <= align if full else True
 
 
 @pytest.mark.parametrize("key,rank", [("c2", 3), ("c2", 0), ("c3", 5)])
