@@ -236,6 +236,56 @@ int prepare_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t 
   return RBA_OK;
 }
 
+// Global position range [lo, hi] of chunk rows [r0, r1) (r0 < r1).
+std::pair<int64_t, int64_t> host_pos_range(const std::vector<Seg>& segs, int64_t r0, int64_t r1) {
+  int64_t lo = INT64_MAX, hi = INT64_MIN;
+  for (const Seg& s : segs) {
+    const int64_t a = std::max(r0, s.row0), b = std::min(r1, s.row0 + s.len);
+    if (a < b) {
+      lo = std::min(lo, s.start + (a - s.row0));
+      hi = std::max(hi, s.start + (b - 1 - s.row0));
+    }
+  }
+  return {lo, hi};
+}
+
+// Start of the document holding position p (host copy of cu_seqlens).
+int64_t host_doc_start(const DocTable& dt, int64_t p) {
+  const int32_t* it = std::upper_bound(dt.cu, dt.cu + dt.n + 1, (int32_t)p);
+  return it[-1];
+}
+
+// Heavy-first order of the row groups of a query-stationary launch: the
+// work of a row group is the number of key rows in its allowed position
+// interval (the interval its workgroup walks: up to the group's last
+// position, from the document start of its first position under the
+// document mask), and groups are sorted by decreasing work (stable).  Left
+// in natural order without a mask (all equal), without the host copy of
+// cu_seqlens, or beyond kMaxOrder groups.
+void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::FwdParams& p, int64_t rows_per_wg) {
+  p.n_order = 0;
+  if (a->mask == RBA_MASK_NONE || p.n_row_groups > rba::kMaxOrder) return;
+  if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu) return;
+  std::vector<std::pair<int64_t, int>> work(p.n_row_groups);
+  for (int rg = 0; rg < p.n_row_groups; ++rg) {
+    const int64_t r0 = rg * rows_per_wg, r1 = std::min(sq, r0 + rows_per_wg);
+    const auto pr = host_pos_range(plan.qs, r0, r1);
+    const int64_t k_hi = pr.second;
+    const int64_t k_lo = a->mask == RBA_MASK_DOC_CAUSAL ? host_doc_start(plan.dt, pr.first) : INT64_MIN;
+    int64_t w = 0;
+    for (const Seg& s : plan.ks) {
+      const int64_t lo = std::max(s.start, k_lo), hi = std::min(s.start + s.len - 1, k_hi);
+      if (hi >= lo) w += hi - lo + 1;
+    }
+    work[rg] = {w, rg};
+  }
+  std::stable_sort(work.begin(), work.end(), [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
+    return x.first > y.first;
+  });
+  for (int i = 0; i < p.n_row_groups; ++i) p.order[i] = (uint16_t)work[i].second;
+  p.n_order = p.n_row_groups;
+}
+
 // Sizes, mask, segments and the launch geometry of the query-stationary
 // kernels (forward step, backward dQ): workgroups of 4 waves, each wave
 // `rows_per_wave` query rows of one head; a workgroup takes 4, 2 or 1 query
@@ -257,6 +307,7 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
+  fill_row_order(a, plan, sq, p, rows_per_wg);
   return RBA_OK;
 }
 

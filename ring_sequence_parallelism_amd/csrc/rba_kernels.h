@@ -9,6 +9,7 @@
 namespace rba {
 
 constexpr int kMaxSegs = 16;
+constexpr int kMaxOrder = 512;   // longest host-computed workgroup order passed in kernel arguments
 
 // A chunk's rows mapped to global positions: rows [row0[s], row0[s+1]) hold
 // positions start[s], start[s]+1, ...  (row0[n] = number of rows).
@@ -41,6 +42,11 @@ struct FwdParams {
   int32_t n_row_groups;
   int32_t n_head_groups;   // hq / hpw
   int32_t n_wg;
+  // Heavy-first order of the row groups (host-computed from the masks and
+  // segments), used when 0 < n_order (== n_row_groups <= kMaxOrder); the
+  // i-th row group a head group's workgroups take is order[i].
+  int32_t n_order;
+  uint16_t order[kMaxOrder];
 };
 
 // Backward step, dK / dV kernel (key-stationary).

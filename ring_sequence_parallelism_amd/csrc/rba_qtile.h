@@ -27,7 +27,8 @@ template <int QR>
 __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int block) {
   const int logical = xcd_remap(block, p.n_wg);
   const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
-  const int rg = logical % p.n_row_groups;
+  const int rg_i = logical % p.n_row_groups;
+  const int rg = p.n_order ? (int)p.order[rg_i] : rg_i;   // heavy first when ordered
   WaveTask t;
   const int hw = wave % p.hpw, rb = wave / p.hpw;
   t.h = hg * p.hpw + hw;
