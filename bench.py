@@ -260,6 +260,23 @@ def main():
                                          "max_segments_per_step": max(tx.kv_segs[i].n for i in tx.kv_segs)}
         del tx
         torch.cuda.empty_cache()
+        # the 32K causal replay under the striped layout (token i on rank i mod 8)
+        import dataclasses
+        wst = dataclasses.replace(W.WORKLOADS["c2"], layout="striped", name="c2_bf16_causal_striped_32k")
+        sx = RingReplay(wst, None, "cuda")
+        sx.forward()
+        torch.cuda.synchronize()
+        tm = LaunchTimer(torch)
+        for _ in range(3):
+            sx.forward(on_step=tm)
+        tm.close()
+        torch.cuda.synchronize()
+        f_ms = sum(ms for kind, _, ms in tm.durations() if kind == "fwd") / 3
+        t = sx.fwd_flops() / (f_ms * 1e-3) / 1e12
+        extra[wst.name] = {"fwd_step_tflops": round(t, 2), "frac_peak": round(t / PEAK_BF16_TFLOPS, 4),
+                           "fwd_ms": round(f_ms, 3)}
+        del sx
+        torch.cuda.empty_cache()
         for key in ("c3", "c4"):
             wx = W.WORKLOADS[key]
             ranks = range(wx.n_ranks) if key == "c3" else [wx.rank]

@@ -72,18 +72,23 @@ typedef enum { RBA_MASK_NONE = 0, RBA_MASK_CAUSAL = 1, RBA_MASK_DOC_CAUSAL = 2 }
 
 /*
  * Chunk offsets: where a chunk's rows sit in the global sequence.  Row r of
- * the chunk has global position start[s] + (r - row0(s)) where s is the
- * segment holding row r and row0(s) = len[0] + ... + len[s-1].  A contiguous
- * split uses one segment, the zigzag split two (pieces r and 2n-1-r), and a
- * TASP step whose KV arrives in slices from several source ranks up to 14.
+ * the chunk has global position start[s] + (r - row0(s)) * stride[s] where s
+ * is the segment holding row r and row0(s) = len[0] + ... + len[s-1].  A
+ * contiguous split uses one segment, the zigzag split two (pieces r and
+ * 2n-1-r), a TASP step whose KV arrives in slices from several source ranks
+ * up to 14, and the striped split (Striped Attention, in the TASP citation
+ * map: token i on rank i mod n) one segment of stride n.
  * Requirements: 1 <= n <= RBA_MAX_SEGS, len[s] >= 1, sum(len) equals the
- * chunk's row count, start[s] >= 0, start[s] + len[s] <= 2^31 - 1, and the
- * segments of one chunk do not overlap in position.
+ * chunk's row count, start[s] >= 0, stride[s] >= 0 (0 is read as 1, so a
+ * zero-initialised struct describes unit-stride runs), the last position
+ * start[s] + (len[s] - 1) * stride[s] <= 2^31 - 1, and the segments of one
+ * chunk share no position.
  */
 typedef struct {
   int32_t n;
   int64_t start[RBA_MAX_SEGS];
   int64_t len[RBA_MAX_SEGS];
+  int64_t stride[RBA_MAX_SEGS];
 } rba_segs;
 
 /* Attention parameters shared by a step's forward and backward. */

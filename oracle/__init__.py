@@ -31,7 +31,7 @@ pages are silent, the reading taken is stated at the function that takes it.
 """
 from .attn import (MASK_NONE, MASK_CAUSAL, MASK_DOC_CAUSAL, allowed_mask, attention,
                         attention_backward, attention_backward_sampled, count_pairs, doc_of, merge, merge_many)
-from .layouts import contiguous_positions, ring_source, zigzag_positions
+from .layouts import contiguous_positions, ring_source, striped_positions, zigzag_positions
 
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_DOC_CAUSAL", "allowed_mask", "attention",

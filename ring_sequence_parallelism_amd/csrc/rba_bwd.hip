@@ -69,11 +69,9 @@ __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_
       it.valid = 0;
       return;
     }
-    const int64_t st = p.qs.start[it.s];
     const int r0 = p.qs.row0[it.s];
-    const int64_t len = p.qs.row0[it.s + 1] - r0;
-    const int64_t a = min(max(q_lo - st, (int64_t)0), len);
-    const int64_t b = min(max(q_hi - st + 1, (int64_t)0), len);
+    const RowSpan rs = rows_in(p.qs.start[it.s], p.qs.stride[it.s], p.qs.row0[it.s + 1] - r0, q_lo, q_hi);
+    const int64_t a = rs.a, b = rs.b;
     if (a >= b) {
       it.qbk = 0;
       it.b1 = 0;
@@ -230,11 +228,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // K^T B operand (row kr = this wave's key `col`) and the transpose-load
   // rows 4 * half.. (A part) and 4 * half + 8.. (B part) of k-step t2 = 0
   // (t2 = 1 is 16 rows further: an immediate offset).
-  const int kr_lane = 32 * wave + col;
-  const uint32_t q_off = row_read_offset<CPR>(col, half);
-  const uint32_t k_off = row_read_offset<CPR>(kr_lane, half);
-  const uint32_t trA = tr_lane_offset<CPR>(4 * half, lane);
-  const uint32_t trB = tr_lane_offset<CPR>(4 * half + 8, lane);
+  // (Recomputed from the lane id in every iteration rather than held in
+  // registers across the loop: the kernel is at its register limit.)
 
   QIter it{-1, 0, 0, 0, 1};
   qiter_next(it, p, q_lo, q_hi);
@@ -262,7 +257,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
 
     if (cls != kSkip) {
       f32x16 sacc = {}, dpacc = {};
-      const uint32_t qo = opaque(q_off), ko = opaque(k_off);
+      const int ln = (int)opaque((uint32_t)lane);
+      const uint32_t qo = row_read_offset<CPR>(ln & 31, ln >> 5);
+      const uint32_t ko = row_read_offset<CPR>(32 * wave + (ln & 31), ln >> 5);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const uint32_t oq = qo ^ (ks << 5), okk = ko ^ (ks << 5);
@@ -288,7 +285,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
             const int qrow = qr0 + qb0 + i;
             bool ok = my_krow < p.sk && qrow < p.sq;
             if (p.mask != kMaskNone) {
-              const int32_t qp = qr.single ? qr.lo + (qrow - qr0) : row_to_pos(p.qs, min(qrow, p.sq - 1));
+              const int32_t qp = qr.single ? qr.lo + (qrow - qr0) * qr.stride : row_to_pos(p.qs, min(qrow, p.sq - 1));
               ok = ok && my_kpos <= qp && qp < my_kend;
             }
             pv = ok ? pv : 0.f;
@@ -298,7 +295,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
         }
       }
       // dV += P^T dO ; dK += dS^T Q  (k-step t2: queries 16*t2 + ...)
-      const uint32_t ta = opaque(trA), tb = opaque(trB);
+      const int ln2 = (int)opaque((uint32_t)lane);
+      const uint32_t ta = tr_lane_offset<CPR>(4 * (ln2 >> 5), ln2);
+      const uint32_t tb = tr_lane_offset<CPR>(4 * (ln2 >> 5) + 8, ln2);
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         u32x4 pw, sw;

@@ -77,6 +77,12 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
+  // Lane offsets in the K / V tiles (XOR-linear swizzle: see row_read_offset
+  // and tr_lane_offset): row `col` for the A operands of S^T and dP^T, and
+  // the transpose-load rows 4*half.. / 4*half + 8.. for K^T.
+  const uint32_t row_off = row_read_offset<CPR>(col, half);
+  const uint32_t tr_a = tr_lane_offset<CPR>(4 * half, lane);
+  const uint32_t tr_b = tr_lane_offset<CPR>(4 * half + 8, lane);
 
   TileIter it{-1, 0, 0, 0, 1};
   tile_next(it, p, t);
@@ -102,12 +108,14 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
       for (int kb = 0; kb < 2; ++kb) {
         // S^T and dP^T for keys kb*32 .. +31 (rows of the A operands).
         f32x16 sacc = {}, dpacc = {};
-        const int r = kb * 32 + col;
+        // rows kb*32 + col: the swizzle ignores row bit 5, so half kb is a
+        // plain byte offset from half 0
+        const uint32_t ro = opaque(row_off);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const int c = ((2 * ks + half) ^ tile_swz<CPR>(r)) << 4;
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt_lds + r * RB + c);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt_lds + r * RB + c);
+          const uint32_t c = ro ^ (ks << 5);
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt_lds + kb * 32 * RB + c);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt_lds + kb * 32 * RB + c);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], sacc, 0, 0, 0);
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dpacc, 0, 0, 0);
         }
@@ -122,14 +130,15 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
         }
         // dQ^T += K^T dS^T.  k-slot of dS^T register j <-> key
         // 16*t2 + 8*(i/4) + 4*half + i%4 (as P^T in the forward's PV).
+        const uint32_t ta = opaque(tr_a), tb = opaque(tr_b);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const u32x4 wv = {w[4 * t2], w[4 * t2 + 1], w[4 * t2 + 2], w[4 * t2 + 3]};
           const bf16x8 b = __builtin_bit_cast(bf16x8, wv);
-          const int rA = kb * 32 + 16 * t2 + 4 * half;
+          const int rA0 = kb * 32 + 16 * t2;   // rows rA0 + 4*half.. (+8): same swizzle as rows 4*half..
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = tr_operand_swz<CPR>(kt_lds, rA, rA + 8, db * 32, lane);
+            const bf16x8 a = tr_read(kt_lds + rA0 * RB, ta ^ (db << 6), tb ^ (db << 6));
             dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dqacc[db], 0, 0, 0);
           }
         }

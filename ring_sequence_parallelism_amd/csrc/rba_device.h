@@ -28,7 +28,7 @@ constexpr int64_t kPosPosInf = int64_t(1) << 40;
 __device__ __forceinline__ int32_t row_to_pos(const SegTable& t, int32_t row) {
   int s = 0;
   while (s + 1 < t.n && row >= t.row0[s + 1]) ++s;
-  return t.start[s] + (row - t.row0[s]);
+  return t.start[s] + (row - t.row0[s]) * t.stride[s];
 }
 
 // Start of the document holding position p: the largest cu[t] <= p, t < n_docs.
@@ -42,26 +42,44 @@ __device__ __forceinline__ int32_t doc_start(const int32_t* cu, int32_t n_docs, 
 }
 
 // Minimum and maximum global position over chunk rows [r0, r1) (r0 < r1),
-// and whether those rows lie in a single segment.
+// and whether those rows lie in a single segment (then row r0 + i is at
+// position lo + i * stride).
 struct PosRange {
   int32_t lo, hi;
   bool single;
+  int32_t stride;
 };
 
 __device__ __forceinline__ PosRange pos_range(const SegTable& t, int32_t r0, int32_t r1) {
-  PosRange out{INT32_MAX, INT32_MIN, true};
+  PosRange out{INT32_MAX, INT32_MIN, true, 1};
   int hits = 0;
   for (int s = 0; s < t.n; ++s) {
     int32_t a = max(r0, t.row0[s]);
     int32_t b = min(r1, t.row0[s + 1]);
     if (a < b) {
       ++hits;
-      out.lo = min(out.lo, t.start[s] + (a - t.row0[s]));
-      out.hi = max(out.hi, t.start[s] + (b - 1 - t.row0[s]));
+      out.lo = min(out.lo, t.start[s] + (a - t.row0[s]) * t.stride[s]);
+      out.hi = max(out.hi, t.start[s] + (b - 1 - t.row0[s]) * t.stride[s]);
+      out.stride = t.stride[s];
     }
   }
   out.single = hits <= 1;
   return out;
+}
+
+// Rows [a, b) of a segment (start st, stride sd, len rows) whose positions
+// lie in [lo, hi]; a >= b when none do.
+struct RowSpan {
+  int64_t a, b;
+};
+__device__ __forceinline__ RowSpan rows_in(int64_t st, int64_t sd, int64_t len, int64_t lo, int64_t hi) {
+  // first row at or after lo, one past the last row at or before hi (floor division)
+  const int64_t da = lo - st, db = hi - st;
+  int64_t a = da <= 0 ? 0 : (da + sd - 1) / sd;
+  int64_t b = db < 0 ? 0 : db / sd + 1;
+  a = min(a, len);
+  b = min(b, len);
+  return RowSpan{a, b};
 }
 
 // 8 XCDs: consecutive workgroup ids are dealt round-robin to the XCDs.  Map
@@ -78,7 +96,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
 // Tile classes.
 constexpr int kSkip = 0, kFull = 1, kPartial = 2;
 
-// Class of a key tile (positions [k.lo, k.hi], `k.single` if contiguous,
+// Class of a key tile (positions [k.lo, k.hi], `k.single` if in one segment,
 // `ragged` if it runs past the end of the chunk) for query rows whose
 // positions lie in [q_lo, q_hi] with document starts in [ds_lo, ds_hi].
 __device__ __forceinline__ int classify(int mask, PosRange k, bool ragged,

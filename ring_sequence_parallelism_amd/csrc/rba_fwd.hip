@@ -274,27 +274,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
             k_lds[(kb * 32 + col) * KST + 2 * ks + half], qreg[ks], sacc[kb], 0, 0, 0);
 
     if (cls == kPartial) {
-      int32_t kp[2][16];
-      if (kr.single) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) kp[kb][j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-      } else {
-        for (int kb = 0; kb < 2; ++kb)
-          for (int j = 0; j < 16; ++j) {
-            const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-            kp[kb][j] = krow < p.sk ? row_to_pos(p.ks, krow) : 0;
-          }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const bool kin = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) < p.sk;
-          const bool ok = kin && visible(p.mask, kp[kb][j], qpos, qds);
-          sacc[kb][j] = ok ? sacc[kb][j] : -INFINITY;
-        }
+      for (int kb = 0; kb < 2; ++kb) mask_block(sacc[kb], p, kr, kr0, kb, half, qpos, qds);
     }
 
     float mx = -INFINITY;

@@ -37,8 +37,36 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Segments
 
 struct Seg {
-  int64_t start, len, row0;
+  int64_t start, len, row0, stride;
+  int64_t last() const { return start + (len - 1) * stride; }   // last position
 };
+
+// Do the position progressions of two segments share a position?  Solved
+// with the Chinese remainder theorem: a0 + i sa = b0 + j sb has solutions
+// x = x0 (mod lcm) iff gcd(sa, sb) divides b0 - a0; then the smallest such x
+// in the intersection of the two ranges decides.
+bool segs_overlap(const Seg& a, const Seg& b) {
+  const int64_t lo = std::max(a.start, b.start), hi = std::min(a.last(), b.last());
+  if (lo > hi) return false;
+  // extended Euclid on (sa, sb)
+  int64_t r0 = a.stride, r1 = b.stride, s0 = 1, s1 = 0;
+  while (r1) {
+    const int64_t q = r0 / r1, t = r0 - q * r1;
+    r0 = r1; r1 = t;
+    const int64_t u = s0 - q * s1;
+    s0 = s1; s1 = u;
+  }
+  const int64_t g = r0;                       // s0 * sa = g (mod sb)
+  const int64_t diff = b.start - a.start;
+  if (diff % g) return false;
+  const int64_t m = b.stride / g;             // solutions i = i0 (mod m)
+  const __int128 i0 = (((__int128)(diff / g) * s0) % m + m) % m;
+  const __int128 L = (__int128)a.stride * m;  // lcm
+  const __int128 x0 = (__int128)a.start + i0 * a.stride;
+  __int128 x = x0;
+  if (x < lo) x += ((lo - x + L - 1) / L) * L;
+  return x <= hi;
+}
 
 // Validates a chunk's segment list against its row count.  rows == 0 allows
 // n == 0.  On success fills `out` (in row order).
@@ -52,20 +80,21 @@ int check_segs(const rba_segs* s, int64_t rows, const char* what, std::vector<Se
   for (int i = 0; i < s->n; ++i) {
     if (s->len[i] < 1) return fail(RBA_ERR_INVALID, "%s: segment %d has length %lld", what, i, (long long)s->len[i]);
     if (s->start[i] < 0) return fail(RBA_ERR_INVALID, "%s: segment %d starts at %lld", what, i, (long long)s->start[i]);
-    if (s->start[i] + s->len[i] > (int64_t)INT32_MAX)
-      return fail(RBA_ERR_UNSUPPORTED, "%s: segment %d reaches position %lld (limit 2^31-1)", what, i,
-                  (long long)(s->start[i] + s->len[i]));
-    out.push_back({s->start[i], s->len[i], total});
+    if (s->stride[i] < 0)
+      return fail(RBA_ERR_INVALID, "%s: segment %d has stride %lld", what, i, (long long)s->stride[i]);
+    const int64_t stride = s->stride[i] ? s->stride[i] : 1;
+    if (stride > (int64_t)INT32_MAX || s->len[i] > (int64_t)INT32_MAX ||
+        s->start[i] + (s->len[i] - 1) * stride >= (int64_t)INT32_MAX)
+      return fail(RBA_ERR_UNSUPPORTED, "%s: segment %d reaches past position 2^31-2", what, i);
+    out.push_back({s->start[i], s->len[i], total, stride});
     total += s->len[i];
   }
   if (total != rows)
     return fail(RBA_ERR_INVALID, "%s: segment lengths sum to %lld, expected %lld rows", what, (long long)total,
                 (long long)rows);
-  std::vector<Seg> sorted = out;
-  std::sort(sorted.begin(), sorted.end(), [](const Seg& a, const Seg& b) { return a.start < b.start; });
-  for (size_t i = 1; i < sorted.size(); ++i)
-    if (sorted[i].start < sorted[i - 1].start + sorted[i - 1].len)
-      return fail(RBA_ERR_INVALID, "%s: segments overlap in position", what);
+  for (size_t i = 0; i < out.size(); ++i)
+    for (size_t j = i + 1; j < out.size(); ++j)
+      if (segs_overlap(out[i], out[j])) return fail(RBA_ERR_INVALID, "%s: segments overlap in position", what);
   return RBA_OK;
 }
 
@@ -75,6 +104,7 @@ rba::SegTable to_table(const std::vector<Seg>& segs) {
   int64_t r = 0;
   for (size_t i = 0; i < segs.size(); ++i) {
     t.start[i] = (int32_t)segs[i].start;
+    t.stride[i] = (int32_t)segs[i].stride;
     t.row0[i] = (int32_t)r;
     r += segs[i].len;
   }
@@ -122,10 +152,19 @@ int check_docs(const rba_attn* a, DocTable& dt) {
 int check_positions_in_docs(const std::vector<Seg>& segs, const DocTable& dt, const char* what) {
   if (!dt.cu) return RBA_OK;
   for (const Seg& s : segs)
-    if (s.start + s.len > dt.cu[dt.n])
+    if (s.last() >= dt.cu[dt.n])
       return fail(RBA_ERR_INVALID, "%s: position %lld is past the packed buffer (%d tokens)", what,
-                  (long long)(s.start + s.len - 1), dt.cu[dt.n]);
+                  (long long)s.last(), dt.cu[dt.n]);
   return RBA_OK;
+}
+
+int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Keys of segment k at positions in [lo, hi].
+int64_t keys_in(const Seg& k, int64_t lo, int64_t hi) {
+  const int64_t b0 = std::max<int64_t>(0, -floor_div(k.start - lo, k.stride));   // first index with pos >= lo
+  const int64_t b1 = std::min<int64_t>(k.len - 1, floor_div(hi - k.start, k.stride));
+  return b1 >= b0 ? b1 - b0 + 1 : 0;
 }
 
 // Exact allowed-pair count of a step (per query head).
@@ -135,6 +174,14 @@ int64_t count_pairs(int mask, const std::vector<Seg>& qs, const std::vector<Seg>
     for (const Seg& k : ks) {
       if (mask == RBA_MASK_NONE) {
         total += q.len * k.len;
+      } else if (q.stride != 1 || k.stride != 1) {
+        // strided positions: per query row, the keys in [doc start, q]
+        for (int64_t a = 0; a < q.len; ++a) {
+          const int64_t qp = q.start + a * q.stride;
+          int64_t lo = INT64_MIN / 4;
+          if (mask == RBA_MASK_DOC_CAUSAL) lo = std::upper_bound(dt.cu, dt.cu + dt.n + 1, (int32_t)qp)[-1];
+          total += keys_in(k, lo, qp);
+        }
       } else if (mask == RBA_MASK_CAUSAL) {
         total += sum_clamp(q.start, q.start + q.len, k.start, k.len);
       } else {
@@ -227,7 +274,7 @@ int prepare_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t 
     if (a->mask == RBA_MASK_CAUSAL) {
       int64_t kmin = INT64_MAX, qmax = INT64_MIN;
       for (const Seg& s : plan.ks) kmin = std::min(kmin, s.start);
-      for (const Seg& s : plan.qs) qmax = std::max(qmax, s.start + s.len - 1);
+      for (const Seg& s : plan.qs) qmax = std::max(qmax, s.last());
       plan.empty = kmin > qmax;
     } else if (a->mask == RBA_MASK_DOC_CAUSAL && plan.dt.cu) {
       plan.empty = count_pairs(a->mask, plan.qs, plan.ks, plan.dt) == 0;
@@ -242,8 +289,8 @@ std::pair<int64_t, int64_t> host_pos_range(const std::vector<Seg>& segs, int64_t
   for (const Seg& s : segs) {
     const int64_t a = std::max(r0, s.row0), b = std::min(r1, s.row0 + s.len);
     if (a < b) {
-      lo = std::min(lo, s.start + (a - s.row0));
-      hi = std::max(hi, s.start + (b - 1 - s.row0));
+      lo = std::min(lo, s.start + (a - s.row0) * s.stride);
+      hi = std::max(hi, s.start + (b - 1 - s.row0) * s.stride);
     }
   }
   return {lo, hi};
@@ -273,10 +320,7 @@ void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fw
     const int64_t k_hi = pr.second;
     const int64_t k_lo = a->mask == RBA_MASK_DOC_CAUSAL ? host_doc_start(plan.dt, pr.first) : INT64_MIN;
     int64_t w = 0;
-    for (const Seg& s : plan.ks) {
-      const int64_t lo = std::max(s.start, k_lo), hi = std::min(s.start + s.len - 1, k_hi);
-      if (hi >= lo) w += hi - lo + 1;
-    }
+    for (const Seg& s : plan.ks) w += keys_in(s, std::max(k_lo, INT64_MIN / 4), k_hi);
     work[rg] = {w, rg};
   }
   std::stable_sort(work.begin(), work.end(), [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {

@@ -12,10 +12,11 @@ constexpr int kMaxSegs = 16;
 constexpr int kMaxOrder = 512;   // longest host-computed workgroup order passed in kernel arguments
 
 // A chunk's rows mapped to global positions: rows [row0[s], row0[s+1]) hold
-// positions start[s], start[s]+1, ...  (row0[n] = number of rows).
+// positions start[s], start[s] + stride[s], ...  (row0[n] = number of rows).
 struct SegTable {
   int32_t n;
   int32_t start[kMaxSegs];
+  int32_t stride[kMaxSegs];
   int32_t row0[kMaxSegs + 1];
 };
 

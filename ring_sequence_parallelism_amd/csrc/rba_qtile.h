@@ -61,11 +61,9 @@ template <typename F>
 __device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask& t, F&& body) {
   int next_tile = 0;
   for (int s = 0; s < p.ks.n; ++s) {
-    const int64_t st = p.ks.start[s];
     const int r0 = p.ks.row0[s];
-    const int64_t len = p.ks.row0[s + 1] - r0;
-    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
-    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    const RowSpan rs = rows_in(p.ks.start[s], p.ks.stride[s], p.ks.row0[s + 1] - r0, t.k_lo, t.k_hi);
+    const int64_t a = rs.a, b = rs.b;
     if (a >= b) continue;
     const int t0 = max((int)((r0 + a) / kBN), next_tile);
     const int t1 = (int)((r0 + b + kBN - 1) / kBN);
@@ -89,11 +87,9 @@ __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, cons
       it.valid = 0;
       return;
     }
-    const int64_t st = p.ks.start[it.s];
     const int r0 = p.ks.row0[it.s];
-    const int64_t len = p.ks.row0[it.s + 1] - r0;
-    const int64_t a = min(max(t.k_lo - st, (int64_t)0), len);
-    const int64_t b = min(max(t.k_hi - st + 1, (int64_t)0), len);
+    const RowSpan rs = rows_in(p.ks.start[it.s], p.ks.stride[it.s], p.ks.row0[it.s + 1] - r0, t.k_lo, t.k_hi);
+    const int64_t a = rs.a, b = rs.b;
     if (a >= b) {
       it.kt = 0;
       it.t1 = 0;
@@ -177,7 +173,7 @@ __device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const 
   int32_t kp[16];
   if (kr.single) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) kp[j] = kr.lo + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+    for (int j = 0; j < 16; ++j) kp[j] = kr.lo + (kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3)) * kr.stride;
   } else {
     for (int j = 0; j < 16; ++j) {
       const int krow = kr0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);

@@ -39,7 +39,8 @@ class RbaError(RuntimeError):
 class rba_segs(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32),
                 ("start", ctypes.c_int64 * RBA_MAX_SEGS),
-                ("len", ctypes.c_int64 * RBA_MAX_SEGS)]
+                ("len", ctypes.c_int64 * RBA_MAX_SEGS),
+                ("stride", ctypes.c_int64 * RBA_MAX_SEGS)]
 
 
 class rba_attn(ctypes.Structure):
@@ -49,15 +50,17 @@ class rba_attn(ctypes.Structure):
                 ("n_docs", ctypes.c_int32)]
 
 
-def make_segs(segments: Sequence[Tuple[int, int]]) -> rba_segs:
-    """[(start, length), ...] in row order -> rba_segs."""
+def make_segs(segments: Sequence[Tuple[int, ...]]) -> rba_segs:
+    """[(start, length) or (start, length, stride), ...] in row order -> rba_segs
+    (stride 1 when omitted)."""
     s = rba_segs()
     if len(segments) > RBA_MAX_SEGS:
         raise ValueError(f"at most {RBA_MAX_SEGS} segments")
     s.n = len(segments)
-    for i, (st, ln) in enumerate(segments):
-        s.start[i] = int(st)
-        s.len[i] = int(ln)
+    for i, seg in enumerate(segments):
+        s.start[i] = int(seg[0])
+        s.len[i] = int(seg[1])
+        s.stride[i] = int(seg[2]) if len(seg) > 2 else 1
     return s
 
 

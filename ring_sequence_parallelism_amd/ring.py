@@ -58,7 +58,7 @@ class RingReplay:
         srcs = sorted(set(self.order if kv_sources is None else kv_sources))
         # inputs
         self.q = to_device(W.gen_rank_chunk(w, W.T_Q, self.r), w.dtype, self.device)
-        self.q_segs = rba.make_segs(w.rank_segments(self.r))
+        self.q_segs = rba.make_segs(w.rank_runs(self.r))
         self.order = self._build_kv(srcs)
         self.cu_host = None
         self.cu_dev = None
@@ -98,7 +98,7 @@ class RingReplay:
         w = self.w
         self.k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in srcs}
         self.v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in srcs}
-        self.kv_segs = {j: rba.make_segs(w.rank_segments(j)) for j in srcs}
+        self.kv_segs = {j: rba.make_segs(w.rank_runs(j)) for j in srcs}
         return self.order
 
     # -- forward -----------------------------------------------------------

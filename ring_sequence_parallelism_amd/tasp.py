@@ -140,28 +140,29 @@ class TaspSchedule:
                 if bounds[c][1] > bounds[c][0]]
 
 
-def slice_segments(w: W.Workload, ref: SliceRef) -> List[Tuple[int, int]]:
-    """Global position segments (start, length) of a slice's rows, in row order."""
+def slice_segments(w: W.Workload, ref: SliceRef) -> List[Tuple[int, int, int]]:
+    """Global position segments (start, length, stride) of a slice's rows, in
+    row order."""
     out = []
     a, b = ref.rows
-    for start, length, row0 in _chunk_runs(w, ref.src):
+    for start, length, stride, row0 in _chunk_runs(w, ref.src):
         lo, hi = max(a, row0), min(b, row0 + length)
         if lo < hi:
-            out.append((start + (lo - row0), hi - lo))
+            out.append((start + (lo - row0) * stride, hi - lo, stride))
     return out
 
 
 def _chunk_runs(w: W.Workload, src: int):
-    """(position start, length, first row) of each position run of chunk `src`."""
+    """(position start, length, stride, first row) of each position run of chunk `src`."""
     row0 = 0
-    for start, length in w.rank_segments(src):
-        yield start, length, row0
+    for start, length, stride in w.rank_runs(src):
+        yield start, length, stride, row0
         row0 += length
 
 
-def step_segments(w: W.Workload, slices: Sequence[SliceRef]) -> List[Tuple[int, int]]:
+def step_segments(w: W.Workload, slices: Sequence[SliceRef]) -> List[Tuple[int, int, int]]:
     """Position segments of a step's assembled KV (slices concatenated in order)."""
-    segs: List[Tuple[int, int]] = []
+    segs: List[Tuple[int, int, int]] = []
     for ref in slices:
         segs.extend(slice_segments(w, ref))
     return segs
@@ -169,4 +170,4 @@ def step_segments(w: W.Workload, slices: Sequence[SliceRef]) -> List[Tuple[int, 
 
 def step_positions(w: W.Workload, slices: Sequence[SliceRef]) -> np.ndarray:
     """Global positions of the assembled KV rows of a step, in row order."""
-    return np.concatenate([np.arange(s, s + n) for s, n in step_segments(w, slices)])
+    return np.concatenate([s + d * np.arange(n) for s, n, d in step_segments(w, slices)])

@@ -19,7 +19,9 @@ Layouts (which pieces a virtual rank holds) follow the workload text of the
 ring-attention pages: a contiguous split gives rank ``r`` piece ``r``; the
 zigzag split of Zigzag-Ring Attention gives rank ``r`` of ``n`` the pieces
 ``r`` and ``2n-1-r`` (TASP pages, experiment highlights: Zigzag-Ring
-Attention is the load-balanced causal variant they compare against).
+Attention is the load-balanced causal variant they compare against); the
+striped split (Striped Attention, TASP citation map) gives rank ``r`` every
+token at a position congruent to ``r`` modulo ``n``.
 """
 from __future__ import annotations
 
@@ -49,7 +51,7 @@ class Workload:
     d: int
     dtype: str          # "bf16" or "f32"
     value_scale: float  # inputs are N(0,1) * value_scale
-    layout: str         # "contiguous" or "zigzag"
+    layout: str         # "contiguous", "zigzag" or "striped"
     mask: int           # MASK_* constant
     rank: int           # the rank whose replay is measured / checked
     backward: bool = False
@@ -79,8 +81,19 @@ class Workload:
         return [r]
 
     def rank_segments(self, r: int) -> List[Tuple[int, int]]:
-        """(start, length) of each contiguous run of global positions, in row order."""
+        """(start, length) of each contiguous run of global positions, in row
+        order (contiguous and zigzag layouts)."""
+        if self.layout == "striped":
+            raise ValueError("a striped chunk is not a union of contiguous runs: use rank_runs")
         return [(p * self.piece_len, self.piece_len) for p in self.rank_pieces(r)]
+
+    def rank_runs(self, r: int) -> List[Tuple[int, int, int]]:
+        """(start, length, stride) of each run of global positions, in row
+        order: the striped layout (token i on rank i mod n) is one run of
+        stride n."""
+        if self.layout == "striped":
+            return [(r, self.chunk_len, self.n_ranks)]
+        return [(s, n, 1) for s, n in self.rank_segments(r)]
 
 
 # The five workloads.  Seeds: workload k uses seed k.
@@ -160,7 +173,11 @@ def gen_pieces(w: Workload, tensor: int, pieces: Sequence[int], threads: int = 8
 
 
 def gen_rank_chunk(w: Workload, tensor: int, r: int, threads: int = 8) -> np.ndarray:
-    """The rows virtual rank ``r`` holds of ``tensor`` (its chunk), in row order."""
+    """The rows virtual rank ``r`` holds of ``tensor`` (its chunk), in row order.
+    A striped chunk takes every n-th row of the whole sequence (generated
+    piecewise as for the contiguous split)."""
+    if w.layout == "striped":
+        return np.ascontiguousarray(gen_pieces(w, tensor, range(w.n_pieces), threads)[r::w.n_ranks])
     return gen_pieces(w, tensor, w.rank_pieces(r), threads)
 
 

@@ -44,6 +44,8 @@ def assert_lse(got, want, what: str):
 def chunk_positions(w: W.Workload, r: int) -> np.ndarray:
     if w.layout == "zigzag":
         return oracle.zigzag_positions(w.seq, w.n_ranks, r)
+    if w.layout == "striped":
+        return oracle.striped_positions(w.seq, w.n_ranks, r)
     return oracle.contiguous_positions(w.seq, w.n_ranks, r)
 
 

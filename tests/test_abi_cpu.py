@@ -35,8 +35,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # rba_segs: int32 n, pad, int64[16], int64[16]; rba_attn ends with n_docs
-    assert ctypes.sizeof(rba.rba_segs) == 8 + 16 * 8 * 2
+    # rba_segs: int32 n, pad, int64 start[16], len[16], stride[16]; rba_attn ends with n_docs
+    assert ctypes.sizeof(rba.rba_segs) == 8 + 16 * 8 * 3
+    assert rba.rba_segs.stride.offset == 8 + 16 * 8 * 2
     assert rba.rba_attn.cu_seqlens_dev.offset == 24
     assert rba.rba_attn.n_docs.offset == 40
 
@@ -239,3 +240,73 @@ def test_fwd_step_acc_validation():
     empty[0] = ctypes.byref(ac)
     empty[7] = ctypes.byref(rba.make_segs([(64, 64)]))       # keys after every query
     assert f(*empty) == rba.RBA_STEP_EMPTY
+
+
+# ---------------------------------------------------------------------------
+# strided segments
+
+def _plan_rc(a, segs):
+    lib = rba.load()
+    pairs = ctypes.c_int64(0)
+    qs = rba.make_segs(segs)
+    return lib.rba_plan_step(ctypes.byref(a), sum(x[1] for x in segs), ctypes.byref(qs), 64,
+                             ctypes.byref(SEG64), ctypes.byref(pairs))
+
+
+def test_strided_segment_overlap_checks():
+    a = _attn(mask=rba.RBA_MASK_NONE)
+    plan = lambda segs: _plan_rc(a, segs)
+    assert plan([(0, 10, 2), (1, 10, 2)]) == rba.RBA_OK              # evens and odds interleave
+    assert plan([(0, 6, 3), (1, 6, 3), (2, 6, 3)]) == rba.RBA_OK
+    for bad in ([(0, 10, 2), (4, 3, 1)],          # 4 is even
+                [(0, 10, 3), (6, 2, 2)],          # 6 = 0 + 2*3
+                [(5, 4, 4), (13, 1, 1)],          # 13 = 5 + 2*4
+                [(0, 5, 6), (9, 5, 4)]):          # 0,6,...,24 vs 9,13,...,25: disjoint
+        rc = _plan_rc(a, bad)
+        share = len(set(_strided_positions(bad))) < sum(x[1] for x in bad)
+        assert (rc == rba.RBA_ERR_INVALID) == share, (bad, rc)
+    assert plan([(0, 5, 6), (3, 5, 6)]) == rba.RBA_OK
+    assert _plan_rc(a, [(0, 4, -1)]) == rba.RBA_ERR_INVALID
+    assert _plan_rc(a, [(2**30, 4, 2**29)]) == rba.RBA_ERR_UNSUPPORTED       # past position 2^31 - 2
+
+
+def _strided_positions(segs):
+    return np.concatenate([s + d * np.arange(n) for s, n, d in segs]) if segs else np.zeros(0, np.int64)
+
+
+@pytest.mark.parametrize("mask", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(5))
+def test_plan_pairs_match_oracle_strided(mask, seed):
+    rng = np.random.default_rng(500 + 10 * mask + seed)
+    # striped query rows of one rank, and strided or contiguous key runs
+    n = int(rng.integers(2, 9))
+    qsegs = [(int(rng.integers(0, n)), int(rng.integers(1, 120)), n)]
+    r0 = int(rng.integers(0, n))
+    ksegs = [(r0, int(rng.integers(1, 80)), n), (int(rng.integers(2000, 2100)), int(rng.integers(1, 50)), 1)]
+    qpos, kpos = _strided_positions(qsegs), _strided_positions(ksegs)
+    end = int(max(qpos.max(), kpos.max())) + 1
+    cu = None
+    if mask == 2:
+        cuts = np.sort(rng.choice(np.arange(1, end), min(12, end - 1), replace=False))
+        cu = np.concatenate([[0], cuts, [end]]).astype(np.int32)
+    a = _attn(mask=mask, cu_seqlens_host=cu)
+    if mask == 2:
+        a.cu_seqlens_dev = 0x20000
+    st, pairs = rba.rba_plan_step(a, qpos.size, rba.make_segs(qsegs), kpos.size, rba.make_segs(ksegs))
+    want = oracle.count_pairs(qpos, kpos, mask, cu)
+    assert pairs == want
+    assert st == (rba.RBA_OK if want else rba.RBA_STEP_EMPTY)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_strided_overlap_matches_brute_force(seed):
+    # the host's progression-intersection test against explicit position sets
+    rng = np.random.default_rng(900 + seed)
+    a = _attn(mask=rba.RBA_MASK_NONE)
+    for _ in range(60):
+        k = int(rng.integers(2, 4))
+        segs = [(int(rng.integers(0, 60)), int(rng.integers(1, 12)), int(rng.integers(1, 9))) for _ in range(k)]
+        pos = _strided_positions(segs)
+        share = len(set(pos.tolist())) < pos.size
+        rc = _plan_rc(a, segs)
+        assert (rc == rba.RBA_ERR_INVALID) == share, segs

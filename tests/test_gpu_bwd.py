@@ -246,3 +246,21 @@ def test_full_ring_backward_scaled():
         assert_close(dq[j].cpu().numpy(), wdq[p], "bf16", f"dq rank {j}")
         assert_close(dk[j].cpu().numpy(), wdk[p], "bf16", f"dk chunk {j}")
         assert_close(dv[j].cpu().numpy(), wdv[p], "bf16", f"dv chunk {j}")
+
+
+def test_replay_striped_scaled():
+    """Backward replay under the striped layout (one stride-n segment per chunk)."""
+    import dataclasses
+    w = dataclasses.replace(W.scaled_workload(W.WORKLOADS["c5"], 4096, hq=8, hkv=2), layout="striped")
+    _say("bwd replay striped", w.name)
+    rr, dq, dk, dv = _replay_grads(w, 6)
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, 6), w.dtype)
+    do64 = W.to_f64(W.gen_rank_chunk(w, W.T_DO, 6), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    wdq, wdk, wdv, *_ = oracle.attention_backward(q64, k64, v64, do64, chunk_positions(w, 6),
+                                                  np.arange(w.seq), w.mask, w.scale)
+    assert_close(dq, wdq, "bf16", "dq")
+    for j in dk:
+        kp = chunk_positions(w, j)
+        assert_close(dk[j], wdk[kp], "bf16", f"dk src {j}")
+        assert_close(dv[j], wdv[kp], "bf16", f"dv src {j}")

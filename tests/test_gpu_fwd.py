@@ -38,7 +38,8 @@ def _segs_for(rng, rows, nseg, gap_max=40, base=0):
 
 
 def _pos(segs):
-    return np.concatenate([np.arange(s, s + n) for s, n in segs])
+    """Positions of (start, length[, stride]) runs, in row order."""
+    return np.concatenate([g[0] + (g[2] if len(g) > 2 else 1) * np.arange(g[1]) for g in segs])
 
 
 def _rand_inputs(rng, n, h, d, dtype):
@@ -372,3 +373,43 @@ def test_replay_merge_paths_agree(fused):
     want_o, want_l = oracle.attention(q64, k64, v64, qpos, np.arange(w.seq), w.mask, w.scale)
     assert_lse(rr.lse_acc.cpu().numpy(), want_l, "lse")
     assert_close(rr.o_final.float().cpu().numpy(), want_o, "bf16", "o")
+
+
+# ---------------------------------------------------------------------------
+# striped layout (strided position segments)
+
+def _striped(w):
+    import dataclasses
+    return dataclasses.replace(w, layout="striped", name=w.name + "_striped")
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_replay_striped_scaled(rank):
+    w = _striped(W.scaled_workload(W.WORKLOADS["c2"], 4096, hq=8, hkv=2))
+    _say("replay", w.name, "rank", rank)
+    _check_replay(w, rank)
+
+
+def test_replay_striped_packed_docs_scaled():
+    w = _striped(W.scaled_workload(W.WORKLOADS["c3"], 8192, hq=8, hkv=2))
+    _say("replay", w.name, "rank", 7)
+    _check_replay(w, 7)
+
+
+@pytest.mark.parametrize("mask", [0, 1, 2])
+@pytest.mark.parametrize("d", [64, 128])
+def test_step_strided_segments(mask, d):
+    """Mixed strided and unit-stride segments on both sides of one step."""
+    _say("fwd strided step", d, "mask", mask)
+    rng = np.random.default_rng(70 + 3 * d + mask)
+    qsegs = [(3, 150, 5), (2000, 60, 1)]
+    ksegs = [(1, 130, 5), (700, 70, 3), (1990, 33, 1)]
+    end = 2100
+    cu = None
+    if mask == 2:
+        cu = np.array([0, 250, 600, 1500, 1995, end], dtype=np.int32)
+    sq, sk = sum(x[1] for x in qsegs), sum(x[1] for x in ksegs)
+    st, o, lse, wo, wl = run_step(rng, sq, sk, 4, 2, d, mask, "bf16", qsegs, ksegs, cu)
+    assert st == rba.RBA_OK
+    assert_lse(lse, wl, "lse")
+    assert_close(o, wo, "bf16", "o_part")

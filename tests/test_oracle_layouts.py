@@ -6,6 +6,8 @@ Pair counts are pinned to closed forms: a zigzag rank with pieces of n_p
 tokens over n ranks has 2 n n_p^2 + n_p causal pairs per head, and a packed
 buffer of documents L_t has sum L_t (L_t + 1) / 2 document-causal pairs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -119,3 +121,38 @@ def test_workload_segments_match_oracle_layouts():
             else:
                 ref = oracle.contiguous_positions(w.seq, w.n_ranks, r)
             assert np.array_equal(pos, ref), (key, r)
+
+
+# ---------------------------------------------------------------------------
+# striped layout (token i on rank i mod n)
+
+@pytest.mark.parametrize("seq,n", [(32, 4), (4096, 8), (96, 3)])
+def test_striped_positions_partition_and_residues(seq, n):
+    allp = np.concatenate([oracle.striped_positions(seq, n, r) for r in range(n)])
+    assert np.array_equal(np.sort(allp), np.arange(seq))
+    for r in range(n):
+        p = oracle.striped_positions(seq, n, r)
+        assert (p % n == r).all() and np.all(np.diff(p) == n)
+
+
+@pytest.mark.parametrize("r", [0, 3, 7])
+def test_striped_causal_pairs_closed_form(r):
+    # rank r's queries against the whole sequence, causal: the row at
+    # position r + n a sees r + n a + 1 keys, so the total is
+    # c (r + 1) + n c (c - 1) / 2 for c = S / n rows
+    seq, n = 512, 8
+    c = seq // n
+    qpos = oracle.striped_positions(seq, n, r)
+    want = c * (r + 1) + n * c * (c - 1) // 2
+    assert oracle.count_pairs(qpos, np.arange(seq), oracle.MASK_CAUSAL) == want
+
+
+def test_striped_workload_chunk_rows():
+    # the generator's striped chunk is every n-th row of the position-ordered sequence
+    w = W.scaled_workload(W.WORKLOADS["c2"], 256, hq=2, hkv=1, d=64)
+    w = dataclasses.replace(w, layout="striped")
+    full = W.gen_pieces(w, W.T_K, range(w.n_pieces))
+    for r in (0, 5):
+        chunk = W.gen_rank_chunk(w, W.T_K, r)
+        assert np.array_equal(chunk, full[oracle.striped_positions(w.seq, w.n_ranks, r)])
+    assert w.rank_runs(5) == [(5, w.chunk_len, w.n_ranks)]
