@@ -135,7 +135,10 @@ int rba_fwd_step(const rba_attn* a,
  * RBA_F32) — the last step of a replay.  o_acc [sq, hq, d] and lse_acc
  * [hq, sq] fp32 are in/out and must already hold a result (the first step
  * of a ring goes through rba_fwd_step).  This saves the partial's round
- * trip through HBM and the merge launch.  Same inputs, limits and errors as
+ * trip through HBM and the merge launch.  A row to which the step shows no
+ * key (LSE_s = -inf) merges as the identity: its o_acc and lse_acc are
+ * neither read nor written, so a row empty on both sides keeps whatever
+ * o_acc holds.  Same inputs, limits and errors as
  * rba_fwd_step; o_final must not alias o_acc.  On RBA_STEP_EMPTY nothing is
  * launched: o_acc / lse_acc are unchanged and o_final is NOT written (finish
  * with rba_merge and no partial).

@@ -215,6 +215,9 @@ __device__ __forceinline__ void write_step_output(const FwdParams& p, int row, i
       }
     return;
   }
+  // An empty partial merges as the identity: the row's running result is
+  // neither read nor written (unless the final output is due).
+  if (lse == -INFINITY && !p.o_final) return;
   f32x4 old[D / 32][4];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)

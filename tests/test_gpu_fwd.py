@@ -343,6 +343,9 @@ def test_fwd_step_acc_equals_step_plus_merge(final, d):
     fin = ~torch.isneginf(l_ref)
     assert torch.allclose(l_acc[fin], l_ref[fin], rtol=1e-6, atol=1e-6)
     assert (o_acc[0:20, 0] == 0).all()                    # empty in both: (0, -inf)
+    # an empty step row merges as the identity, bit for bit
+    assert torch.equal(o_acc[0:20, 1:], acc0[0:20, 1:])
+    assert torch.equal(l_acc[1:, 0:20], lse0[1:, 0:20])
     assert torch.isneginf(l_acc[0, 0:20]).all()
     assert torch.allclose(o_acc[20:30, 0], o_part[20:30, 0], rtol=1e-6, atol=1e-6)   # empty accumulator
     if final:
