@@ -59,6 +59,7 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, in
 struct QIter {
   int s, qbk, b1, next_blk;
   int valid;   // int, not bool: a padding-free struct stays in registers
+  int seg_r0, seg_r1, seg_st, seg_sd;   // rows [seg_r0, seg_r1), first position and stride of segment s
 };
 
 __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_t q_lo, int64_t q_hi) {
@@ -70,7 +71,11 @@ __device__ __forceinline__ void qiter_next(QIter& it, const BwdParams& p, int64_
       return;
     }
     const int r0 = p.qs.row0[it.s];
-    const RowSpan rs = rows_in(p.qs.start[it.s], p.qs.stride[it.s], p.qs.row0[it.s + 1] - r0, q_lo, q_hi);
+    it.seg_r0 = r0;
+    it.seg_r1 = p.qs.row0[it.s + 1];
+    it.seg_st = p.qs.start[it.s];
+    it.seg_sd = p.qs.stride[it.s];
+    const RowSpan rs = rows_in(it.seg_st, it.seg_sd, it.seg_r1 - r0, q_lo, q_hi);
     const int64_t a = rs.a, b = rs.b;
     if (a >= b) {
       it.qbk = 0;
@@ -248,7 +253,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     qiter_next(nx, p, q_lo, q_hi);
     if (nx.valid) issue(nx, buf ^ 1);
 
-    const PosRange qr = pos_range(p.qs, qr0, qr1);
+    const PosRange qr = (qr0 >= it.seg_r0 && qr1 <= it.seg_r1)
+                            ? PosRange{it.seg_st + (qr0 - it.seg_r0) * it.seg_sd,
+                                       it.seg_st + (qr1 - 1 - it.seg_r0) * it.seg_sd, true, it.seg_sd}
+                            : pos_range(p.qs, qr0, qr1);
     int cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
     const bool q_ragged = qr1 - qr0 < kBQ;
     if (cls == kFull && q_ragged) cls = kPartial;

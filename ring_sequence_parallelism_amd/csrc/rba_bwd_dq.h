@@ -99,7 +99,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
     tile_next(nx, p, t);
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
-    const PosRange kr = pos_range(p.ks, kr0, kr1);
+    const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
     const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
     if (cls != kSkip) {
       const char* kt_lds = lds[buf][0];

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     tile_next(nx, p, t);
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
-    const PosRange kr = pos_range(p.ks, kr0, kr1);
+    const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
     const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
     if (cls != kSkip) {
       const char* kt_lds = lds[buf][0];

@@ -77,6 +77,7 @@ __device__ __forceinline__ void for_each_tile(const FwdParams& p, const WaveTask
 struct TileIter {
   int s, kt, t1, next_tile;
   int valid;   // int, not bool: a padding-free struct stays in registers
+  int seg_r0, seg_r1, seg_st, seg_sd;   // rows [seg_r0, seg_r1), first position and stride of segment s
 };
 
 __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, const WaveTask& t) {
@@ -88,7 +89,11 @@ __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, cons
       return;
     }
     const int r0 = p.ks.row0[it.s];
-    const RowSpan rs = rows_in(p.ks.start[it.s], p.ks.stride[it.s], p.ks.row0[it.s + 1] - r0, t.k_lo, t.k_hi);
+    it.seg_r0 = r0;
+    it.seg_r1 = p.ks.row0[it.s + 1];
+    it.seg_st = p.ks.start[it.s];
+    it.seg_sd = p.ks.stride[it.s];
+    const RowSpan rs = rows_in(it.seg_st, it.seg_sd, it.seg_r1 - r0, t.k_lo, t.k_hi);
     const int64_t a = rs.a, b = rs.b;
     if (a >= b) {
       it.kt = 0;
@@ -99,6 +104,16 @@ __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, cons
     it.t1 = (int)((r0 + b + kBN - 1) / kBN);
     it.next_tile = max(it.next_tile, it.t1);
   }
+}
+
+// Position range of key rows [r0, r1) of the tile the iterator is on: from
+// the current segment's fields when the rows lie inside it (the common case),
+// else from the segment table.
+__device__ __forceinline__ PosRange tile_pos_range(const TileIter& it, const SegTable& t, int r0, int r1) {
+  if (r0 >= it.seg_r0 && r1 <= it.seg_r1)
+    return PosRange{it.seg_st + (r0 - it.seg_r0) * it.seg_sd, it.seg_st + (r1 - 1 - it.seg_r0) * it.seg_sd, true,
+                    it.seg_sd};
+  return pos_range(t, r0, r1);
 }
 
 // Direct-to-LDS loads of K and V key tiles (kBN rows of one KV head) into
