@@ -18,7 +18,11 @@
 //     for the whole pass over the 32-row query blocks that can see those
 //     keys.  Splitting the group's query heads over workgroups balances the
 //     causal work (low key tiles see every query block); the group's partial
-//     dK / dV are summed with fp32 atomics into zeroed outputs.  Workgroups
+//     dK / dV are summed with fp32 atomics into zeroed outputs.  When every
+//     key tile sees the same query rows (a chunk wholly before or after the
+//     queries, or no mask) and there are workgroups to spare, a workgroup
+//     instead takes several heads of the group in turn and sums them in its
+//     accumulators (all of them: plain stores, no zero fill).  Workgroups
 //     are ordered KV head, key tile, query head, so the heavier low key tiles
 //     are dispatched first on every XCD.
 //   * Scores are computed as S = Q K^T (v_mfma_f32_32x32x16_bf16) so a lane
@@ -126,17 +130,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int col = lane & 31, half = lane >> 5;
   const int logical = xcd_remap(wg, p.n_wg);
-  const int g = logical / (p.n_key_tiles * p.group);
-  const int kt = (logical / p.group) % p.n_key_tiles;
-  const int h = g * p.group + logical % p.group;   // the query head of this workgroup
+  const int sets = p.group / p.heads_per_wg;      // workgroups per key tile
+  const int g = logical / (p.n_key_tiles * sets);
+  const int kt = (logical / sets) % p.n_key_tiles;
+  const int h0 = g * p.group + (logical % sets) * p.heads_per_wg;   // first query head of this workgroup
   const int kr0 = kt * kBK;
   const int kr1 = min(kr0 + kBK, p.sk);
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
   // Uniform bases of this workgroup's heads and 32-bit row strides in bytes
   // (q, dO and k are each smaller than 4 GiB, checked on the host).
   const uint32_t q_row_bytes = (uint32_t)p.hq * RB, k_row_bytes = (uint32_t)p.hkv * RB;
-  const char* qg = uniform_ptr(static_cast<const char*>(p.q) + (uint32_t)(h * RB));
-  const char* dog = uniform_ptr(static_cast<const char*>(p.d_o) + (uint32_t)(h * RB));
+  const char* qg = nullptr;
+  const char* dog = nullptr;
   const char* kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(g * RB));
 
   // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
@@ -199,8 +204,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     qoff[i] = (uint32_t)r * q_row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
   }
   const uint32_t qd_wave = lds_addr(&qd_lds[0][0][0]) + wave * QLOADS * 1024;
-  const float* lse_h = p.lse + (size_t)h * p.sq;
-  const float* dlt_h = p.delta + (size_t)h * p.sq;
+  const float* lse_h = nullptr;
+  const float* dlt_h = nullptr;
   auto issue = [&](const QIter& b, int buf) {
     const int qr0 = b.qbk * kBQ;
     const uint32_t dst = qd_wave + buf * 2 * QT;
@@ -236,9 +241,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // (Recomputed from the lane id in every iteration rather than held in
   // registers across the loop: the kernel is at its register limit.)
 
-  QIter it{-1, 0, 0, 0, 1};
-  qiter_next(it, p, q_lo, q_hi);
-  if (it.valid) issue(it, 0);
+  QIter it{};
   // One query block, for a compile-time buffer index (the loop is unrolled
   // by two so LDS addresses of either buffer are immediate offsets).
   auto block = [&](auto buf_c) {
@@ -328,16 +331,30 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     }
     it = nx;
   };
-  while (it.valid) {
-    block(std::integral_constant<int, 0>{});
-    if (!it.valid) break;
-    block(std::integral_constant<int, 1>{});
+  // The workgroup's query heads one after another, their dK / dV summed in
+  // the accumulators.
+  for (int hh = 0; hh < p.heads_per_wg; ++hh) {
+    const int h = h0 + hh;
+    qg = uniform_ptr(static_cast<const char*>(p.q) + (uint32_t)(h * RB));
+    dog = uniform_ptr(static_cast<const char*>(p.d_o) + (uint32_t)(h * RB));
+    lse_h = p.lse + (size_t)h * p.sq;
+    dlt_h = p.delta + (size_t)h * p.sq;
+    // every wave is done with the previous head's buffers
+    if (hh > 0) __syncthreads();
+    it = QIter{-1, 0, 0, 0, 1};
+    qiter_next(it, p, q_lo, q_hi);
+    if (it.valid) issue(it, 0);
+    while (it.valid) {
+      block(std::integral_constant<int, 0>{});
+      if (!it.valid) break;
+      block(std::integral_constant<int, 1>{});
+    }
   }
 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).
-  // With one query head per KV head the workgroup owns its keys' gradients
-  // and stores (or adds) them; otherwise the group's workgroups add with
-  // atomics, into zeroed outputs or into the accumulators.
+  // When the workgroup sums every query head of the group it owns its keys'
+  // gradients and stores (or adds) them; otherwise the group's workgroups add
+  // with atomics, into zeroed outputs or into the accumulators.
   if (!wave_any) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -347,10 +364,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
       if (krow < p.sk) {
         float* dkp = p.dk + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
         float* dvp = p.dv + ((size_t)krow * p.hkv + g) * D + db * 32 + col;
-        if (p.group == 1 && !p.accumulate) {
+        if (p.heads_per_wg == p.group && !p.accumulate) {
           *dkp = dkacc[db][j] * p.scale;
           *dvp = dvacc[db][j];
-        } else if (p.group == 1) {
+        } else if (p.heads_per_wg == p.group) {
           *dkp += dkacc[db][j] * p.scale;
           *dvp += dvacc[db][j];
         } else {

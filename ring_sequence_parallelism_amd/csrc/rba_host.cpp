@@ -244,6 +244,19 @@ int check_device() {
   return RBA_OK;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(RBA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
   return RBA_OK;
@@ -471,6 +484,37 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32
 
 namespace {
 
+// Query heads a dK / dV workgroup sums over.  Summing several heads of a GQA
+// group in one workgroup replaces their atomic adds (and, with the whole
+// group, the zero fill) but makes fewer, longer workgroups, so it is used
+// only when every key tile sees the same number of query rows (one long
+// workgroup cannot be balanced by the heavy-first order) and there are still
+// enough workgroups to give every CU two.
+int choose_heads_per_wg(const rba_attn* a, const StepPlan& plan, int64_t sk, int bk) {
+  const int group = a->hq / a->hkv;
+  if (group == 1) return 1;
+  if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu) return 1;
+  const int64_t tiles = (sk + bk - 1) / bk;
+  int64_t lo_rows = INT64_MAX, hi_rows = 0;
+  for (int64_t t = 0; t < tiles; ++t) {
+    const auto pr = host_pos_range(plan.ks, t * bk, std::min<int64_t>((t + 1) * bk, sk));
+    int64_t q_lo = INT64_MIN / 4, q_hi = INT64_MAX / 4;
+    if (a->mask != RBA_MASK_NONE) q_lo = pr.first;
+    if (a->mask == RBA_MASK_DOC_CAUSAL)
+      q_hi = (int64_t)*std::upper_bound(plan.dt.cu, plan.dt.cu + plan.dt.n + 1, (int32_t)pr.second) - 1;
+    int64_t rows = 0;
+    for (const Seg& q : plan.qs) rows += keys_in(q, q_lo, q_hi);
+    lo_rows = std::min(lo_rows, rows);
+    hi_rows = std::max(hi_rows, rows);
+  }
+  if (lo_rows != hi_rows) return 1;
+  const int64_t slots = 2 * (int64_t)device_cus();
+  int best = 1;
+  for (int hpw = 2; hpw <= group; ++hpw)
+    if (group % hpw == 0 && tiles * a->hq / hpw >= slots) best = hpw;
+  return best;
+}
+
 // Shared body of rba_bwd_step (dK / dV overwritten) and rba_bwd_step_acc
 // (dK / dV added into accumulators).
 int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
@@ -505,10 +549,11 @@ int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
   p.ks = to_table(plan.ks);
   const int bk = rba::bwd_keys_per_wg(a->d);
   p.n_key_tiles = (int32_t)((sk + bk - 1) / bk);
-  const int64_t n_wg = (int64_t)p.n_key_tiles * a->hq;
+  p.heads_per_wg = choose_heads_per_wg(a, plan, sk, bk);
+  const int64_t n_wg = (int64_t)p.n_key_tiles * a->hq / p.heads_per_wg;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
-  if (p.group > 1 && !accumulate) {
+  if (p.heads_per_wg < p.group && !accumulate) {
     // the group's workgroups add their partial dK / dV into zeroed outputs
     hipError_t e = rba::launch_zero_f32(dk, dv, sk * a->hkv * a->d, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "backward zero fill");

@@ -69,7 +69,8 @@ struct BwdParams {
   int32_t n_docs;
   SegTable qs, ks;
   int32_t n_key_tiles;
-  int32_t n_wg;      // n_key_tiles * hkv * group: one workgroup per (key tile, query head)
+  int32_t heads_per_wg;   // query heads of a group one workgroup sums over (divides group)
+  int32_t n_wg;      // n_key_tiles * hkv * group / heads_per_wg: one workgroup per (key tile, head set)
 };
 
 // Backward dQ kernel: the query-stationary geometry of a forward step (the

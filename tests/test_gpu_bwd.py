@@ -57,6 +57,12 @@ STEP_CASES = [
     (96, 257, 6, 2, 128, [(257, 96)], [(0, 200), (400, 57)], 0),
     (130, 200, 8, 2, 128, [(100, 130)], [(0, 200)], 2),
     (1, 70, 4, 1, 128, [(69, 1)], [(0, 70)], 1),
+    # every key tile sees every query row, and there are enough tiles for the
+    # dK / dV workgroups to sum several query heads of a group (on a 256-CU
+    # device): all four heads (no atomics, no zero fill) without a mask, two
+    # heads under the causal mask
+    (64, 8192, 32, 8, 128, [(0, 64)], [(0, 8192)], 0),
+    (64, 4096, 32, 8, 128, [(10_000, 64)], [(0, 4096)], 1),
 ]
 
 
@@ -185,12 +191,14 @@ def test_replay_c5_full_sampled():
 # ---------------------------------------------------------------------------
 # KV-side accumulation (rba_bwd_step_acc)
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2)])
-def test_step_acc_adds_into_accumulators(hq, hkv):
-    """rba_bwd_step_acc adds exactly what rba_bwd_step writes (bit for bit with
-    one query head per KV head, where each element is added once)."""
-    sq, sk, d = 200, 333, 128
-    _say("bwd step acc", hq, hkv)
+@pytest.mark.parametrize("hq,hkv,sq,sk,q0", [(4, 4, 200, 333, 100), (8, 2, 200, 333, 100),
+                                              (32, 8, 64, 8192, 8192)])
+def test_step_acc_adds_into_accumulators(hq, hkv, sq, sk, q0):
+    """rba_bwd_step_acc adds exactly what rba_bwd_step writes (bit for bit when
+    each element is added once: one query head per KV head, or, in the large
+    case, workgroups that sum all heads of a group in registers)."""
+    d = 128
+    _say("bwd step acc", hq, hkv, sq, sk)
     rng = np.random.default_rng(hq * 10 + hkv)
     qb, _ = _bf16(rng, (sq, hq, d))
     kb, _ = _bf16(rng, (sk, hkv, d))
@@ -199,7 +207,7 @@ def test_step_acc_adds_into_accumulators(hq, hkv):
     scale = float(np.float32(1 / np.sqrt(d)))
     a = rba.attn_params(hq, hkv, d, scale, rba.RBA_BF16, rba.RBA_MASK_CAUSAL)
     q, k, v, dO = (to_device(x, "bf16", DEV) for x in (qb, kb, vb, dob))
-    qs, ks = rba.make_segs([(100, sq)]), rba.make_segs([(0, sk)])
+    qs, ks = rba.make_segs([(q0, sq)]), rba.make_segs([(0, sk)])
     o = torch.empty((sq, hq, d), device=DEV)
     lse = torch.empty((hq, sq), device=DEV)
     assert rba.rba_fwd_step(a, q, qs, k, v, ks, o, lse) == rba.RBA_OK
@@ -216,14 +224,14 @@ def test_step_acc_adds_into_accumulators(hq, hkv):
     assert rba.rba_bwd_step_acc(a, q, qs, k, v, ks, dO, lse, delta, dq2, dk2, dv2) == rba.RBA_OK
     torch.cuda.synchronize()
     assert torch.equal(dq1, dq2)
-    if hq == hkv:
+    if hq == hkv or sk == 8192:
         assert torch.equal(dk2, base_k + dk1) and torch.equal(dv2, base_v + dv1)
     else:
         assert torch.allclose(dk2, base_k + dk1, rtol=1e-5, atol=1e-5)
         assert torch.allclose(dv2, base_v + dv1, rtol=1e-5, atol=1e-5)
     # an empty step leaves the accumulators untouched
     before = dk2.clone()
-    st = rba.rba_bwd_step_acc(a, q, qs, k, v, rba.make_segs([(10_000, sk)]), dO, lse, delta, dq2, dk2, dv2)
+    st = rba.rba_bwd_step_acc(a, q, qs, k, v, rba.make_segs([(q0 + 10_000, sk)]), dO, lse, delta, dq2, dk2, dv2)
     torch.cuda.synchronize()
     assert st == rba.RBA_STEP_EMPTY and torch.equal(dk2, before)
 
