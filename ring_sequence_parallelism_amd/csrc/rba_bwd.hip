@@ -144,16 +144,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   const char* dog = nullptr;
   const char* kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(g * RB));
 
-  // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
-#pragma unroll
-  for (int i = 0; i < kBK / ROWS_PER_LOAD / 4; ++i) {
-    const int ld = wave * (kBK / ROWS_PER_LOAD / 4) + i;
-    const int r = ld * ROWS_PER_LOAD + lane / CPR;
-    const int c = (lane % CPR) ^ tile_swz<CPR>(r);
-    const uint32_t krow = (uint32_t)min(kr0 + r, p.sk - 1);
-    dma16(kg, krow * k_row_bytes + (uint32_t)(c << 4), lds_addr(k_lds) + ld * 1024);
-  }
-
   // This wave's 32 keys: rows kr0 + 32*wave + col.
   const int wk0 = kr0 + 32 * wave;
   const int wk1 = min(wk0 + 32, p.sk);
@@ -162,9 +152,33 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   if (wave_any) wkr = pos_range(p.ks, wk0, wk1);
   const bool wave_ragged = wk1 - wk0 < 32;
 
+  // Query positions that can see a key of this tile; a workgroup with no
+  // query block in that range loads nothing (and, unless it must store its
+  // zero gradients, writes nothing).
+  const PosRange tkr = pos_range(p.ks, kr0, kr1);
+  int64_t q_lo = kPosNegInf, q_hi = kPosPosInf;
+  if (p.mask != kMaskNone) q_lo = tkr.lo;
+  if (p.mask == kMaskDoc) q_hi = (int64_t)doc_end(p.cu, p.n_docs, tkr.hi) - 1;
+  QIter first{-1, 0, 0, 0, 1};
+  qiter_next(first, p, q_lo, q_hi);
+  const bool stores = p.heads_per_wg == p.group && !p.accumulate;
+  if (!first.valid && !stores) return;
+
+  // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
+  if (first.valid) {
+#pragma unroll
+    for (int i = 0; i < kBK / ROWS_PER_LOAD / 4; ++i) {
+      const int ld = wave * (kBK / ROWS_PER_LOAD / 4) + i;
+      const int r = ld * ROWS_PER_LOAD + lane / CPR;
+      const int c = (lane % CPR) ^ tile_swz<CPR>(r);
+      const uint32_t krow = (uint32_t)min(kr0 + r, p.sk - 1);
+      dma16(kg, krow * k_row_bytes + (uint32_t)(c << 4), lds_addr(k_lds) + ld * 1024);
+    }
+  }
+
   // V rows as B operands of dP = dO V^T (lane: key col, d = 16*ks + 8*half + 0..7).
-  bf16x8 vreg[D / 16];
-  {
+  bf16x8 vreg[D / 16] = {};
+  if (first.valid) {
     const int krow = min(wk0 + col, p.sk - 1);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(vbase + ((size_t)krow * p.hkv + g) * D);
 #pragma unroll
@@ -185,12 +199,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
-
-  // Query positions that can see a key of this tile.
-  const PosRange tkr = pos_range(p.ks, kr0, kr1);
-  int64_t q_lo = kPosNegInf, q_hi = kPosPosInf;
-  if (p.mask != kMaskNone) q_lo = tkr.lo;
-  if (p.mask == kMaskDoc) q_hi = (int64_t)doc_end(p.cu, p.n_docs, tkr.hi) - 1;
 
   // Direct-to-LDS loads of query block b into buffer `buf`: Q and dO rows
   // (rows past the end re-read the last row and are masked) and, from wave
@@ -242,6 +250,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // registers across the loop: the kernel is at its register limit.)
 
   QIter it{};
+  int visited = 0;   // some block of this wave had allowed pairs (wave-uniform)
   // One query block, for a compile-time buffer index (the loop is unrolled
   // by two so LDS addresses of either buffer are immediate offsets).
   auto block = [&](auto buf_c) {
@@ -267,6 +276,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     const char* dot = qd_lds[buf][1];
 
     if (cls != kSkip) {
+      visited = 1;
       f32x16 sacc = {}, dpacc = {};
       const int ln = (int)opaque((uint32_t)lane);
       const uint32_t qo = row_read_offset<CPR>(ln & 31, ln >> 5);
@@ -341,8 +351,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     dlt_h = p.delta + (size_t)h * p.sq;
     // every wave is done with the previous head's buffers
     if (hh > 0) __syncthreads();
-    it = QIter{-1, 0, 0, 0, 1};
-    qiter_next(it, p, q_lo, q_hi);
+    it = first;
     if (it.valid) issue(it, 0);
     while (it.valid) {
       block(std::integral_constant<int, 0>{});
@@ -354,8 +363,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // dK = scale * acc, dV = acc for this wave's keys (rows: keys 8*(j/4)+4*half+j%4).
   // When the workgroup sums every query head of the group it owns its keys'
   // gradients and stores (or adds) them; otherwise the group's workgroups add
-  // with atomics, into zeroed outputs or into the accumulators.
-  if (!wave_any) return;
+  // with atomics, into zeroed outputs or into the accumulators (a wave that
+  // saw no allowed pair has nothing to add).
+  if (!wave_any || (!visited && !stores)) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -46,6 +46,10 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const WaveTask t = make_task<32>(p, wave, block);
+  // A workgroup whose rows see no key tile adds nothing to dq_acc.
+  TileIter it{-1, 0, 0, 0, 1};
+  tile_next(it, p, t);
+  if (!it.valid) return;
   const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
 
   // Q^T and dO^T as B operands: lane holds query `col`, d = 16*ks + 8*half + 0..7.
@@ -84,9 +88,8 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
   const uint32_t tr_a = tr_lane_offset<CPR>(4 * half, lane);
   const uint32_t tr_b = tr_lane_offset<CPR>(4 * half + 8, lane);
 
-  TileIter it{-1, 0, 0, 0, 1};
-  tile_next(it, p, t);
-  if (it.valid) loader.issue(it.kt, 0);
+  int visited = 0;   // some tile of this wave had allowed pairs (wave-uniform)
+  loader.issue(it.kt, 0);
   auto tile = [&](auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     const int kt = it.kt;
@@ -102,6 +105,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
     const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
     const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
     if (cls != kSkip) {
+      visited = 1;
       const char* kt_lds = lds[buf][0];
       const char* vt_lds = lds[buf][1];
 #pragma unroll
@@ -154,7 +158,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
 
   // dq_acc[row, h, :] += scale * dQ^T[:, row] (accumulator rows: d =
   // 32*db + 8*(j/4) + 4*half + j%4, four consecutive d per f32x4).
-  if (row_ok) {
+  if (row_ok && visited) {
     float* dst = dp.dq + ((size_t)row * p.hq + t.h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

@@ -49,6 +49,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
   const int col = lane & 31, half = lane >> 5;
   const WaveTask t = make_task<QR>(p, wave, blockIdx.x);
+  TileIter it{-1, 0, 0, 0, 1};
+  tile_next(it, p, t);
+  // A merging step whose rows see no key tile leaves the running result as
+  // it is (an empty partial merges as the identity).
+  if (!it.valid && p.accumulate && !p.o_final) return;
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -80,8 +85,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  TileIter it{-1, 0, 0, 0, 1};
-  tile_next(it, p, t);
   if (it.valid) loader.issue(it.kt, 0);
   // The body of one key tile, for a compile-time buffer index (the loop is
   // unrolled by two so LDS addresses of either buffer are immediate offsets).

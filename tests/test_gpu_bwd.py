@@ -63,6 +63,7 @@ STEP_CASES = [
     # heads under the causal mask
     (64, 8192, 32, 8, 128, [(0, 64)], [(0, 8192)], 0),
     (64, 4096, 32, 8, 128, [(10_000, 64)], [(0, 4096)], 1),
+    (40, 8192, 32, 8, 64, [(9_000, 40)], [(0, 8192)], 1),
 ]
 
 
