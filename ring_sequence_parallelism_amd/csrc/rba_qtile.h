@@ -185,6 +185,24 @@ struct KvLoader {
 // into the vector).
 __device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const PosRange& kr, int kr0, int kb,
                                            int half, int32_t qpos, int32_t qd) {
+  if (kr.single && kr.stride == 1) {
+    // Contiguous positions: element j holds tile row base + c_j (c_j = 8 (j / 4)
+    // + j % 4) at position kr.lo + base + c_j, so the mask is a window
+    // lo <= c_j <= hi on the lane's row offsets.
+    const int base = kb * 32 + 4 * half;
+    int hi = p.sk - 1 - kr0 - base;                       // inside the chunk
+    int lo = INT32_MIN;
+    if (p.mask != kMaskNone) {
+      hi = qpos == kPosNone ? -1 : min(hi, qpos - kr.lo - base);   // at or before the query
+      if (p.mask == kMaskDoc) lo = qd - kr.lo - base;                // in the query's document
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = 8 * (j >> 2) + (j & 3);
+      s[j] = (c <= hi && c >= lo) ? s[j] : -INFINITY;
+    }
+    return;
+  }
   int32_t kp[16];
   if (kr.single) {
 #pragma unroll
