@@ -114,7 +114,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
         f32x16 sacc = {}, dpacc = {};
         // rows kb*32 + col: the swizzle ignores row bit 5, so half kb is a
         // plain byte offset from half 0
-        const uint32_t ro = opaque(row_off);
+        const uint32_t ro = row_off;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const uint32_t c = ro ^ (ks << 5);
@@ -134,7 +134,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
         }
         // dQ^T += K^T dS^T.  k-slot of dS^T register j <-> key
         // 16*t2 + 8*(i/4) + 4*half + i%4 (as P^T in the forward's PV).
-        const uint32_t ta = opaque(tr_a), tb = opaque(tr_b);
+        const uint32_t ta = tr_a, tb = tr_b;
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const u32x4 wv = {w[4 * t2], w[4 * t2 + 1], w[4 * t2 + 2], w[4 * t2 + 3]};
