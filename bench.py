@@ -18,6 +18,7 @@ counted) / time of the step, with all inputs resident in HBM.
 
 Prints ONE JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--extra] [--flush-mib 512]
 """
 from __future__ import annotations
 
@@ -46,6 +47,9 @@ def parse():
                     help="also time the forward replays of the 64K packed-document and 512K zigzag workloads")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows in the CPU-oracle sample")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="also time steps with the last-level cache flushed before each one "
+                         "(a MIB-sized device buffer is overwritten between steps, outside the timing)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 4 device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -179,15 +183,19 @@ def main():
     timer = LaunchTimer(torch)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        marks[k].record()
         run_step(rr, timer)
+    marks[-1].record()
     timer.close()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    step_ms = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
 
     # per-kernel time over the timed region
     per = {}
@@ -239,7 +247,29 @@ def main():
         "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "effective_pairs_per_head": rr.effective_pairs,
         "step_effective_flops": step_flops,
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+        "step_ms_min": round(step_ms[0], 4),
     }
+    if args.flush_mib > 0:
+        # cold last-level cache: overwrite a buffer larger than the 256 MB
+        # Infinity Cache before each step, then time the step alone
+        buf = torch.empty(args.flush_mib * (1 << 18), dtype=torch.float32, device="cuda")
+        cold = []
+        for k in range(args.steps):
+            buf.fill_(float(k))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_step(rr)
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        cold.sort()
+        med = cold[len(cold) // 2]
+        breakdown["cold_cache"] = {"flush_mib": args.flush_mib, "step_ms_median": round(med, 4),
+                                   "step_ms_min": round(cold[0], 4),
+                                   "tflops_at_median": round(step_flops / (med * 1e-3) / 1e12, 2)}
+        del buf
+        torch.cuda.empty_cache()
     extra = {}
     if args.extra:
         # the same 32K zigzag forward under TASP's decomposed schedule: steps
