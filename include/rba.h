@@ -186,11 +186,14 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32
  *   q, d_o [sq, hq, d] (dtype); k, v [sk, hkv, d] (dtype); lse, delta
  *   [hq, sq] fp32; dq_acc [sq, hq, d] fp32; dk_step, dv_step [sk, hkv, d] fp32.
  * On RBA_STEP_EMPTY nothing is launched: dq_acc is unchanged and dk_step /
- * dv_step are NOT written (the step's true dK/dV are zero).  Two kernels run
- * on `stream`: a key-stationary one for dk_step / dv_step (with more than one
- * query head per KV head, the heads' parts are summed with fp32 atomics into
- * the zero-filled outputs, so their low bits depend on scheduling) and a
- * query-stationary one that adds each dq_acc row once (deterministic).
+ * dv_step are NOT written (the step's true dK/dV are zero).  One kernel runs
+ * on `stream` (after a zero fill of dk_step / dv_step when needed), holding
+ * a key-stationary pass for dk_step / dv_step and a query-stationary pass
+ * that adds each dq_acc row once (deterministic).  With more than one query
+ * head per KV head, a dK / dV workgroup sums one or several heads of the
+ * group in registers; when it does not sum the whole group, the group's
+ * parts are added with fp32 atomics into the zero-filled outputs, so their
+ * low bits depend on scheduling.
  * dtype RBA_BF16 only, d in {64, 128}; q, d_o, k and v must each be smaller
  * than 4 GiB, else RBA_ERR_UNSUPPORTED.
  */
@@ -209,9 +212,11 @@ int rba_bwd_step(const rba_attn* a,
  * attention definition sums dK_j, dV_j over all queries; TASP abstract,
  * training in HSAP methodology).  No zero fill is launched.  Same arguments,
  * layouts, limits and errors as rba_bwd_step; on RBA_STEP_EMPTY nothing is
- * launched and the accumulators are unchanged.  With more than one query
- * head per KV head the additions are fp32 atomics (low bits depend on
- * scheduling); with one, each element is read, added and written once.
+ * launched and the accumulators are unchanged.  When a dK / dV workgroup
+ * sums every query head of its group (one head per KV head, or the host's
+ * choice for steps where every key tile sees the same query rows), each
+ * element is read, added and written once; otherwise the additions are fp32
+ * atomics (low bits depend on scheduling).
  */
 int rba_bwd_step_acc(const rba_attn* a,
                      const void* q, int64_t sq, const rba_segs* q_segs,

@@ -9,7 +9,8 @@
 //   dS_ij = P_ij (<dO_i, v_j> - delta_i)
 //   dK_j  = scale * sum_i dS_ij q_i
 // summing dK / dV over the query heads that share a KV head (GQA).  dQ is
-// computed by the query-stationary kernel in rba_bwd_dq.hip.
+// computed by the query-stationary pass in rba_bwd_dq.h; both passes run in
+// one launch (bwd_kernel below).
 //
 // gfx950 design
 //   * A workgroup owns 128 keys of one KV head and one query head of its
