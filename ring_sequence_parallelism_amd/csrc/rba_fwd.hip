@@ -102,8 +102,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
     const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
-    const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
-    if (cls != kSkip) {
+    // A tile this wave may skip (another wave of the workgroup needs it) is
+    // computed fully masked instead: no branch around the tile body.
+    const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    const int cls = cls0 == kSkip ? kPartial : cls0;
+    {
       const char* kt_lds = lds[buf][0];
       const char* vt_lds = lds[buf][1];
       // S^T = K Q^T for two 32-key blocks.
