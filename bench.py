@@ -93,11 +93,17 @@ class LaunchTimer:
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bwd_step_32k_zigzag_hbm_traffic.md")
 
 
+# Sources that make up rba_bwd_step (host planning and launch, the fused
+# backward kernel and the headers it includes): the counter summary is only
+# valid for the code it was measured on.
+BWD_SOURCES = ("rba_host.cpp", "rba_bwd.hip", "rba_bwd_dq.h", "rba_qtile.h", "rba_device.h", "rba_kernels.h")
+
+
 def kernel_sources_sha256():
     import hashlib
     src = os.path.join(ROOT, "ring_sequence_parallelism_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(f for f in os.listdir(src) if f.endswith((".hip", ".h", ".cpp"))):
+    for f in sorted(BWD_SOURCES):
         h.update(f.encode())
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
