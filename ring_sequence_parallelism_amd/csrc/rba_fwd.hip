@@ -25,8 +25,10 @@
 //     read as the A operand of PV through the LDS transpose load, in the
 //     key order the P^T accumulator rows imply.  One barrier per tile.
 //   * Key tiles outside the allowed position interval of the workgroup are
-//     never visited; inside it, each wave classifies a tile as skipped,
-//     full (no mask arithmetic) or partial (per-element mask).
+//     never visited; inside it, each wave classifies a tile as full (no mask
+//     arithmetic) or partial (per-element mask; a tile wholly masked for
+//     one wave but needed by another is computed masked, so the tile body
+//     has no branch around it).
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score,
 //     and a lazy running maximum that rarely rescales O.
 #include <type_traits>
