@@ -75,6 +75,8 @@ struct RowSpan {
 __device__ __forceinline__ RowSpan rows_in(int64_t st, int64_t sd, int64_t len, int64_t lo, int64_t hi) {
   // first row at or after lo, one past the last row at or before hi (floor division)
   const int64_t da = lo - st, db = hi - st;
+  if (sd == 1)   // contiguous positions: no division
+    return RowSpan{min(max(da, (int64_t)0), len), min(max(db + 1, (int64_t)0), len)};
   int64_t a = da <= 0 ? 0 : (da + sd - 1) / sd;
   int64_t b = db < 0 ? 0 : db / sd + 1;
   a = min(a, len);
