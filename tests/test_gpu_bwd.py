@@ -115,9 +115,9 @@ def _replay_grads(w, rank):
     return rr, dq.cpu().numpy(), {j: t.cpu().numpy() for j, t in dk.items()}, {j: t.cpu().numpy() for j, t in dv.items()}
 
 
-@pytest.mark.parametrize("rank", [0, 3])
-def test_replay_zigzag_scaled(rank):
-    w = W.scaled_workload(W.WORKLOADS["c5"], 4096)
+@pytest.mark.parametrize("rank,d", [(0, 128), (3, 128), (5, 64)])
+def test_replay_zigzag_scaled(rank, d):
+    w = W.scaled_workload(W.WORKLOADS["c5"], 4096, d=d, name=f"c5_s4096_d{d}")
     _say("bwd replay", w.name, "rank", rank)
     rr, dq, dk, dv = _replay_grads(w, rank)
     q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, rr.r), w.dtype)

@@ -254,6 +254,14 @@ def test_replay_zigzag_scaled(rank):
     _check_replay(w, rank)
 
 
+@pytest.mark.parametrize("rank", [2, 6])
+def test_replay_zigzag_scaled_d64(rank):
+    # head_dim 64 through the whole replay (merging epilogue included)
+    w = W.scaled_workload(W.WORKLOADS["c2"], 4096, d=64, name="c2_s4096_d64")
+    _say("replay", w.name, "rank", rank)
+    _check_replay(w, rank)
+
+
 @pytest.mark.parametrize("rank", [0, 9, 15])
 def test_replay_packed_docs_scaled(rank):
     w = W.scaled_workload(W.WORKLOADS["c3"], 8192, hq=8, hkv=2)
