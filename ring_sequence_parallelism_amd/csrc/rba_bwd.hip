@@ -115,7 +115,9 @@ constexpr int dkdv_lds_bytes() { return kBK * D * 2 + 2 * 2 * kBQ * D * 2 + 2 * 
 
 // One workgroup (4 waves, number `wg` of p.n_wg) of the dK / dV pass, with
 // `smem` the workgroup's LDS (dkdv_lds_bytes<D>() bytes, 16-byte aligned).
-template <int D>
+// FULL: every visited (key wave, query block) pair is full (shown on the
+// host), so blocks need no classification and no per-element mask.
+template <int D, bool FULL>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* smem) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
@@ -186,10 +188,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     for (int ks = 0; ks < D / 16; ++ks) vreg[ks] = src[2 * ks + half];
   }
   const int my_krow = wk0 + col;
-  const int32_t my_kpos = my_krow < p.sk ? row_to_pos(p.ks, my_krow) : INT32_MAX;
+  const int32_t my_kpos = (my_krow < p.sk && !FULL) ? row_to_pos(p.ks, my_krow) : INT32_MAX;
   // document ends (document mask): of this lane's key and of the wave's key range
   int32_t my_kend = INT32_MAX, wkend_lo = INT32_MAX, wkend_hi = INT32_MAX;
-  if (p.mask == kMaskDoc) {
+  if (!FULL && p.mask == kMaskDoc) {
     if (my_krow < p.sk) my_kend = doc_end(p.cu, p.n_docs, my_kpos);
     if (wave_any) {
       wkend_lo = doc_end(p.cu, p.n_docs, wkr.lo);
@@ -266,13 +268,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     qiter_next(nx, p, q_lo, q_hi);
     if (nx.valid) issue(nx, buf ^ 1);
 
-    const PosRange qr = (qr0 >= it.seg_r0 && qr1 <= it.seg_r1)
-                            ? PosRange{it.seg_st + (qr0 - it.seg_r0) * it.seg_sd,
-                                       it.seg_st + (qr1 - 1 - it.seg_r0) * it.seg_sd, true, it.seg_sd}
-                            : pos_range(p.qs, qr0, qr1);
-    int cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
-    const bool q_ragged = qr1 - qr0 < kBQ;
-    if (cls == kFull && q_ragged) cls = kPartial;
+    PosRange qr{0, 0, true, 1};
+    int cls = wave_any ? kFull : kSkip;
+    if (!FULL) {
+      qr = (qr0 >= it.seg_r0 && qr1 <= it.seg_r1)
+               ? PosRange{it.seg_st + (qr0 - it.seg_r0) * it.seg_sd,
+                          it.seg_st + (qr1 - 1 - it.seg_r0) * it.seg_sd, true, it.seg_sd}
+               : pos_range(p.qs, qr0, qr1);
+      cls = classify_keys(p.mask, wkr, wave_ragged || !wkr.single, wkend_lo, wkend_hi, qr, wave_any);
+      const bool q_ragged = qr1 - qr0 < kBQ;
+      if (cls == kFull && q_ragged) cls = kPartial;
+    }
     const char* qt = qd_lds[buf][0];
     const char* dot = qd_lds[buf][1];
 
@@ -303,7 +309,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * j4 + i;
           float pv = fast_exp2(fmaf(sacc[j], p.scale_log2, -l4[i] * 1.4426950408889634f));
-          if (cls == kPartial) {
+          if (!FULL && cls == kPartial) {
             const int qrow = qr0 + qb0 + i;
             bool ok = my_krow < p.sk && qrow < p.sq;
             if (p.mask != kMaskNone) {
@@ -415,23 +421,29 @@ int bwd_keys_per_wg(int d) {
 // pass (heaviest key tiles first), the following dp.f.n_wg the dQ pass, which
 // fills the CUs as the dK / dV tail drains.  The two passes share no output
 // and read the same inputs.  LDS is one buffer sized for the larger body.
-template <int D>
+// FULL: both passes visit only full tiles / blocks (shown on the host).
+template <int D, bool FULL>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kernel(BwdParams p, DqParams dp) {
   constexpr int SMEM = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int b = blockIdx.x;
   if (b < p.n_wg)
-    bwd_dkdv_body<D>(p, b, smem);
+    bwd_dkdv_body<D, FULL>(p, b, smem);
   else
-    bwd_dq_body<D>(dp, b - p.n_wg, smem);
+    bwd_dq_body<D, FULL>(dp, b - p.n_wg, smem);
 }
 
 hipError_t launch_bwd(const BwdParams& p, const DqParams& dp, int d, hipStream_t s) {
   dim3 grid(p.n_wg + dp.f.n_wg), block(kBwdThreads);
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_kernel<128>, grid, block, 0, s, p, dp);
+  const bool full = p.all_full && dp.f.all_full;
+  if (d == 128 && full)
+    hipLaunchKernelGGL((bwd_kernel<128, true>), grid, block, 0, s, p, dp);
+  else if (d == 128)
+    hipLaunchKernelGGL((bwd_kernel<128, false>), grid, block, 0, s, p, dp);
+  else if (d == 64 && full)
+    hipLaunchKernelGGL((bwd_kernel<64, true>), grid, block, 0, s, p, dp);
   else if (d == 64)
-    hipLaunchKernelGGL(bwd_kernel<64>, grid, block, 0, s, p, dp);
+    hipLaunchKernelGGL((bwd_kernel<64, false>), grid, block, 0, s, p, dp);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -34,7 +34,9 @@ constexpr int dq_lds_bytes() { return 2 * 2 * kBN * D * 2; }
 
 // One workgroup (4 waves, number `block` of dp.f.n_wg) of the dQ pass, with
 // `smem` the workgroup's LDS (dq_lds_bytes<D>() bytes, 16-byte aligned).
-template <int D>
+// FULL: every visited tile is full for every wave (shown on the host), so
+// tiles need no classification and no mask.
+template <int D, bool FULL>
 __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char* smem) {
   const FwdParams& p = dp.f;
   constexpr int CPR = D / 8;
@@ -67,8 +69,8 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
       doreg[ks] = row_ok ? ds[2 * ks + half] : z;
     }
   }
-  const int32_t qpos = row_ok ? row_to_pos(p.qs, row) : kPosNone;
-  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos) : INT32_MIN;
+  const int32_t qpos = (row_ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
+  const int32_t qds = (row_ok && !FULL && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos) : INT32_MIN;
   // LSE in base 2 (rows without any allowed key, LSE = -inf, get P = 0 like
   // rows past the chunk), and delta.
   float lse2 = INFINITY, dlt = 0.f;
@@ -102,8 +104,12 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
     tile_next(nx, p, t);
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
-    const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
-    const int cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    PosRange kr{0, 0, true, 1};
+    int cls = t.wave_any ? kFull : kSkip;
+    if (!FULL) {
+      kr = tile_pos_range(it, p.ks, kr0, kr1);
+      cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+    }
     if (cls != kSkip) {
       visited = 1;
       const char* kt_lds = lds[buf][0];
@@ -123,7 +129,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], sacc, 0, 0, 0);
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dpacc, 0, 0, 0);
         }
-        if (cls == kPartial) mask_block(sacc, p, kr, kr0, kb, half, qpos, qds);
+        if (!FULL && cls == kPartial) mask_block(sacc, p, kr, kr0, kb, half, qpos, qds);
         // dS^T in place, packed to bf16 pairs in accumulator order.
         uint32_t w[8];
 #pragma unroll

@@ -37,7 +37,9 @@
 
 namespace rba {
 
-template <int D, int NQB>
+// FULL: every visited tile is full for every wave (shown on the host), so
+// the tile body has no classification and no mask code.
+template <int D, int NQB, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int QR = 32 * NQB;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       bf16x8 z = {};
       qreg[qb][ks] = ok ? src[2 * ks + half] : z;
     }
-    qpos[qb] = ok ? row_to_pos(p.qs, row) : kPosNone;
-    qds[qb] = (ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
+    qpos[qb] = (ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
+    qds[qb] = (ok && !FULL && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
   }
 
   const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
@@ -103,11 +105,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     tile_next(nx, p, t);
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
-    const PosRange kr = tile_pos_range(it, p.ks, kr0, kr1);
     // A tile this wave may skip (another wave of the workgroup needs it) is
     // computed fully masked instead: no branch around the tile body.
-    const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
-    const int cls = cls0 == kSkip ? kPartial : cls0;
+    PosRange kr{0, 0, true, 1};
+    int cls = kFull;
+    if (!FULL) {
+      kr = tile_pos_range(it, p.ks, kr0, kr1);
+      const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+      cls = cls0 == kSkip ? kPartial : cls0;
+    }
     {
       const char* kt_lds = lds[buf][0];
       const char* vt_lds = lds[buf][1];
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         }
       }
 
-      if (cls == kPartial) {
+      if (!FULL && cls == kPartial) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -342,10 +348,14 @@ int fwd_rows_per_wave(int d, int dtype_bf16) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
   dim3 grid(p.n_wg), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB>), grid, block, 0, s, p);
+  if (d == 128 && p.all_full)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, true>), grid, block, 0, s, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, false>), grid, block, 0, s, p);
+  else if (d == 64 && p.all_full)
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, true>), grid, block, 0, s, p);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, false>), grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -343,6 +343,33 @@ void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fw
   p.n_order = p.n_row_groups;
 }
 
+// Does every key tile that a query-stationary workgroup visits hold only
+// pairs that the mask allows for every row of the workgroup (and no row past
+// the chunk, and rows of one segment)?  A workgroup of rows with positions
+// in [wlo, whi] visits, in each KV segment, the tiles of the rows at
+// positions up to whi (causal); they are all full when none of those keys
+// lies after wlo and the visited rows end on a tile boundary (or at the end
+// of the segment).  Without a mask every tile is full unless it is ragged.
+// The document mask is never taken as full.
+bool all_tiles_full(const rba_attn* a, const StepPlan& plan, int64_t sq, int64_t sk, int64_t rows_per_wg) {
+  constexpr int64_t BN = rba::kFwdTileKeys;
+  if (a->mask == RBA_MASK_DOC_CAUSAL || sk % BN) return false;
+  if (a->mask == RBA_MASK_NONE) return true;
+  for (const Seg& k : plan.ks)
+    if (k.row0 % BN || k.len % BN) return false;
+  for (int64_t r0 = 0; r0 < sq; r0 += rows_per_wg) {
+    const auto w = host_pos_range(plan.qs, r0, std::min(sq, r0 + rows_per_wg));
+    for (const Seg& k : plan.ks) {
+      // visited rows: positions start + i * stride <= whi
+      const int64_t v = w.second < k.start ? 0 : std::min(k.len, (w.second - k.start) / k.stride + 1);
+      if (v == 0) continue;
+      if (k.start + (v - 1) * k.stride > w.first) return false;
+      if (v < k.len && v % BN) return false;
+    }
+  }
+  return true;
+}
+
 // Sizes, mask, segments and the launch geometry of the query-stationary
 // kernels (forward step, backward dQ): workgroups of 4 waves, each wave
 // `rows_per_wave` query rows of one head; a workgroup takes 4, 2 or 1 query
@@ -365,6 +392,7 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
   fill_row_order(a, plan, sq, p, rows_per_wg);
+  p.all_full = all_tiles_full(a, plan, sq, sk, rows_per_wg) ? 1 : 0;
   return RBA_OK;
 }
 
@@ -515,6 +543,35 @@ int choose_heads_per_wg(const rba_attn* a, const StepPlan& plan, int64_t sk, int
   return best;
 }
 
+// Key-stationary counterpart of all_tiles_full for the dK / dV pass: is every
+// (32-key wave, 32-row query block) pair that a workgroup of `bk` keys
+// visits full?  A workgroup whose keys have positions in [klo, khi] visits,
+// in each query segment, the blocks of the rows at positions from klo on
+// (causal); they are all full when the first such row starts a block (or
+// the segment) and lies at or after khi.  Query blocks and key waves must be
+// whole (no ragged block or wave) and lie in one segment.  The document mask
+// is never taken as full.
+bool all_blocks_full(const rba_attn* a, const StepPlan& plan, int64_t sq, int64_t sk, int64_t bk) {
+  constexpr int64_t BQ = 32, WK = 32;
+  if (a->mask == RBA_MASK_DOC_CAUSAL || sq % BQ || sk % WK) return false;
+  for (const Seg& k : plan.ks)
+    if (k.row0 % WK || k.len % WK) return false;
+  if (a->mask == RBA_MASK_NONE) return true;
+  for (const Seg& q : plan.qs)
+    if (q.row0 % BQ || q.len % BQ) return false;
+  for (int64_t r0 = 0; r0 < sk; r0 += bk) {
+    const auto kr = host_pos_range(plan.ks, r0, std::min(sk, r0 + bk));
+    for (const Seg& q : plan.qs) {
+      // first visited row: the first position >= klo
+      const int64_t a0 = kr.first <= q.start ? 0 : (kr.first - q.start + q.stride - 1) / q.stride;
+      if (a0 >= q.len) continue;
+      if (a0 % BQ) return false;
+      if (q.start + a0 * q.stride < kr.second) return false;
+    }
+  }
+  return true;
+}
+
 // Shared body of rba_bwd_step (dK / dV overwritten) and rba_bwd_step_acc
 // (dK / dV added into accumulators).
 int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
@@ -553,16 +610,18 @@ int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
   const int64_t n_wg = (int64_t)p.n_key_tiles * a->hq / p.heads_per_wg;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
-  if (p.heads_per_wg < p.group && !accumulate) {
-    // the group's workgroups add their partial dK / dV into zeroed outputs
-    hipError_t e = rba::launch_zero_f32(dk, dv, sk * a->hkv * a->d, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "backward zero fill");
-  }
+  p.all_full = all_blocks_full(a, plan, sq, sk, bk) ? 1 : 0;
   rba::DqParams dp{};
   dp.f.q = q; dp.f.k = k; dp.f.v = v;
   if ((rc = fill_query_tiling(a, sq, sk, plan, 32, dp.f))) return rc;
   dp.d_o = d_o; dp.lse = lse; dp.delta = delta; dp.dq = dq_acc; dp.scale = a->scale;
   if ((int64_t)p.n_wg + dp.f.n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
+  // every check is done: launches from here on
+  if (p.heads_per_wg < p.group && !accumulate) {
+    // the group's workgroups add their partial dK / dV into zeroed outputs
+    hipError_t e = rba::launch_zero_f32(dk, dv, sk * a->hkv * a->d, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "backward zero fill");
+  }
   return hip_status(rba::launch_bwd(p, dp, a->d, (hipStream_t)stream), "backward step");
 }
 

@@ -9,7 +9,8 @@
 namespace rba {
 
 constexpr int kMaxSegs = 16;
-constexpr int kMaxOrder = 512;   // longest host-computed workgroup order passed in kernel arguments
+constexpr int kMaxOrder = 512;
+constexpr int kFwdTileKeys = 64;   // keys per tile of the query-stationary kernels   // longest host-computed workgroup order passed in kernel arguments
 
 // A chunk's rows mapped to global positions: rows [row0[s], row0[s+1]) hold
 // positions start[s], start[s] + stride[s], ...  (row0[n] = number of rows).
@@ -48,6 +49,10 @@ struct FwdParams {
   // i-th row group a head group's workgroups take is order[i].
   int32_t n_order;
   uint16_t order[kMaxOrder];
+  // 1: the host has shown that every key tile a workgroup visits is full
+  // (no masked pair, inside the chunk, in one segment) for every wave of it,
+  // so the kernel needs no tile classification and no per-element mask.
+  int32_t all_full;
 };
 
 // Backward step, dK / dV kernel (key-stationary).
@@ -70,6 +75,9 @@ struct BwdParams {
   SegTable qs, ks;
   int32_t n_key_tiles;
   int32_t heads_per_wg;   // query heads of a group one workgroup sums over (divides group)
+  // 1: the host has shown that every (key wave, query block) pair a
+  // workgroup visits is full, so the pass needs no classification or mask.
+  int32_t all_full;
   int32_t n_wg;      // n_key_tiles * hkv * group / heads_per_wg: one workgroup per (key tile, head set)
 };
 

@@ -10,7 +10,7 @@ namespace rba {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = kFwdTileKeys;  // keys per tile
 
 // Which rows and head a wave owns, and the
 // allowed key interval of the workgroup.

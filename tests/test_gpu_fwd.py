@@ -424,3 +424,38 @@ def test_step_strided_segments(mask, d):
     assert st == rba.RBA_OK
     assert_lse(lse, wl, "lse")
     assert_close(o, wo, "bf16", "o_part")
+
+
+# Steps whose every visited key tile is full for every query row (tile-aligned
+# KV segments wholly before the rows that see them, or no mask and whole
+# tiles): the host launches the forward without tile classification or mask
+# code.  Each case also gives the same KV positions split at a row that is
+# not a tile boundary, which takes the general path; both must match the
+# oracle, and each other bit for bit (the arithmetic is the same).
+FULL_CASES = [
+    # mask, d, q segments, k segments, the same keys split off a tile boundary
+    (1, 128, [(4096, 256)], [(0, 512)], [(0, 100), (100, 412)]),
+    (1, 128, [(1024, 128), (3072, 128)], [(512, 256), (2048, 256)], [(512, 37), (549, 219), (2048, 256)]),
+    (1, 64, [(1024, 128), (3072, 128)], [(512, 256), (2048, 256)], [(512, 256), (2048, 70), (2118, 186)]),
+    (1, 128, [(2048, 64, 8), (4000, 96)], [(1, 64, 4), (300, 128)], [(1, 30, 4), (121, 34, 4), (300, 128)]),
+    (0, 128, [(0, 100)], [(5000, 128), (0, 64)], None),
+]
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+@pytest.mark.parametrize("case", FULL_CASES, ids=lambda c: f"m{c[0]}d{c[1]}k{len(c[3])}")
+def test_step_full_tiles_path(case, hq, hkv):
+    mask, d, qsegs, ksegs, ksplit = case
+    _say("fwd full-tile path", case, hq, hkv)
+    sq, sk = sum(x[1] for x in qsegs), sum(x[1] for x in ksegs)
+    seed = 90 + d + 7 * mask + hq
+    st, o, lse, wo, wl = run_step(np.random.default_rng(seed), sq, sk, hq, hkv, d, mask, "bf16", qsegs, ksegs)
+    assert st == rba.RBA_OK
+    assert_lse(lse, wl, "lse")
+    assert_close(o, wo, "bf16", "o_part")
+    if ksplit is None:
+        return
+    assert sum(x[1] for x in ksplit) == sk and np.array_equal(_pos(ksplit), _pos(ksegs))
+    st2, o2, lse2, _, _ = run_step(np.random.default_rng(seed), sq, sk, hq, hkv, d, mask, "bf16", qsegs, ksplit)
+    assert st2 == rba.RBA_OK
+    assert np.array_equal(o2, o) and np.array_equal(lse2, lse)
