@@ -305,6 +305,73 @@ __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, uint3
       : "memory");
 }
 
+// A whole K and V tile pair of direct-to-LDS loads (same ordering contract
+// as dma16): load i of K reads kbase + off[i] and lands at LDS byte address
+// lds_k + 1024 * i + 16 * lane, and likewise for V at lds_v.  One M0 save
+// and restore for all of them, M0 stepped by 1 KiB between loads (each M0
+// write is followed by the wait state the load needs).  N is 2 or 4.
+template <int N>
+__device__ __forceinline__ void dma16_kv(const void* kbase_in, const void* vbase_in, const uint32_t (&off)[N],
+                                         uint32_t lds_k_in, uint32_t lds_v_in) {
+  const char* kbase = uniform_ptr(kbase_in);
+  const char* vbase = uniform_ptr(vbase_in);
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_k_in);
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane(lds_v_in);
+  uint32_t saved;
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %5\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %5\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %5\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %6\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(kbase), "s"(vbase), "s"(lds_k), "s"(lds_v)
+        : "memory", "scc");
+  } else {
+    static_assert(N == 2, "2 or 4 loads per tensor");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %4\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off[0]), "v"(off[1]), "s"(kbase), "s"(vbase), "s"(lds_k), "s"(lds_v)
+        : "memory", "scc");
+  }
+}
+
 // Direct-to-LDS load of 4 bytes per lane in the scalar-base form: lane l
 // reads sbase + voff and its dword lands at LDS byte address lds + 4 * l
 // (sbase, lds uniform).  Same ordering contract as dma16.

@@ -142,6 +142,7 @@ struct KvLoader {
   uint32_t row_bytes;   // stride of a K/V row in global memory
   int sk, r_lane;
   uint32_t loff0;       // lane offset of load 0 inside a tile
+  uint32_t loffs[LOADS];   // lane offset of load i from the tile's first row
   uint32_t lds_wave;    // LDS byte address of this wave's part of buffer 0's K tile
 
   __device__ __forceinline__ KvLoader(const FwdParams& p, int g, int wave, int lane, uint32_t lds_base) {
@@ -151,6 +152,11 @@ struct KvLoader {
     sk = p.sk;
     r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;
     loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
+    // the swizzle step only touches the chunk bits, below the row stride
+    // (a multiple of 256 bytes), so the row step adds independently
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      loffs[i] = (loff0 ^ ((uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4)) + (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
     lds_wave = lds_base + wave * LOADS * 1024;
   }
 
@@ -158,6 +164,12 @@ struct KvLoader {
   __device__ __forceinline__ void issue(int kt, int b) const {
     const uint32_t dst = lds_wave + b * 2 * TILE;
     const bool whole = (kt + 1) * kBN <= sk;
+    if (whole) {
+      // one scalar base per tensor; the row steps are in the lane offsets
+      const size_t tb = (size_t)kt * kBN * row_bytes;
+      dma16_kv<LOADS>(kg + tb, vg + tb, loffs, dst, dst + TILE);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       size_t tb = ((size_t)kt * kBN + i * ROWS_PER_LOAD) * row_bytes;
