@@ -250,7 +250,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // rows 4 * half.. (A part) and 4 * half + 8.. (B part) of k-step t2 = 0
   // (t2 = 1 is 16 rows further: an immediate offset).
   // (Recomputed from the lane id in every iteration rather than held in
-  // registers across the loop: the kernel is at its register limit.)
+  // registers across the loop: the general instantiation is at its register
+  // limit.  The full-block one holds the transpose-load offsets, which
+  // leaves it at 246 VGPRs; holding the others too would spill.)
 
   QIter it{};
   int visited = 0;   // some block of this wave had allowed pairs (wave-uniform)
@@ -323,7 +325,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
         }
       }
       // dV += P^T dO ; dK += dS^T Q  (k-step t2: queries 16*t2 + ...)
-      const int ln2 = (int)opaque((uint32_t)lane);
+      const int ln2 = FULL ? lane : (int)opaque((uint32_t)lane);
       const uint32_t ta = tr_lane_offset<CPR>(4 * (ln2 >> 5), ln2);
       const uint32_t tb = tr_lane_offset<CPR>(4 * (ln2 >> 5) + 8, ln2);
 #pragma unroll
