@@ -135,6 +135,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
             sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[kb][qb], 0, 0, 0);
         }
       }
+      if (NQB == 1) {
+        // 6 K reads in flight ahead of the score MFMAs (2 by the compiler's
+        // own schedule, which leaves the MFMAs waiting on LDS latency)
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      }
 
       if (!FULL && cls == kPartial) {
 #pragma unroll
