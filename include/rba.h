@@ -234,6 +234,21 @@ int rba_bwd_step_acc(const rba_attn* a,
 int rba_plan_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs,
                   int64_t sk, const rba_segs* kv_segs, int64_t* pairs);
 
+/*
+ * rba_step_full_tiles — host-only (no device access): whether the step's
+ * launches take the kernels compiled without tile classification and mask
+ * code.  *fwd_full = 1 when every key tile that a forward workgroup visits
+ * holds only pairs the mask allows for every row of that workgroup;
+ * *bwd_full = 1 when the same holds for the dQ pass and, for the dK/dV pass,
+ * every query block a workgroup of keys visits is allowed for all of its
+ * keys.  These are launch choices of this library (the results are the same
+ * either way); the call exists so that the decision can be checked against
+ * an enumeration of the visited tiles.  The document mask always gives 0.
+ * Returns RBA_OK, or an error for invalid arguments (as rba_plan_step).
+ */
+int rba_step_full_tiles(const rba_attn* a, int64_t sq, const rba_segs* q_segs,
+                        int64_t sk, const rba_segs* kv_segs, int32_t* fwd_full, int32_t* bwd_full);
+
 /* Thread-local description of the last error on this thread ("" if none).
  * Valid until the next rba_* call on the same thread. */
 const char* rba_last_error(void);

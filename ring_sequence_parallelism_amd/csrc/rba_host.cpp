@@ -370,6 +370,13 @@ bool all_tiles_full(const rba_attn* a, const StepPlan& plan, int64_t sq, int64_t
   return true;
 }
 
+// Query heads of a query-stationary workgroup (4 waves): 4, 2 or 1 heads of
+// one KV head, times 4 / that many row blocks.
+int query_heads_per_wg(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1); }
+int64_t query_rows_per_wg(int group, int rows_per_wave) {
+  return (int64_t)(4 / query_heads_per_wg(group)) * rows_per_wave;
+}
+
 // Sizes, mask, segments and the launch geometry of the query-stationary
 // kernels (forward step, backward dQ): workgroups of 4 waves, each wave
 // `rows_per_wave` query rows of one head; a workgroup takes 4, 2 or 1 query
@@ -383,9 +390,9 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   p.n_docs = a->mask == RBA_MASK_DOC_CAUSAL ? a->n_docs : 0;
   p.qs = to_table(plan.qs);
   p.ks = to_table(plan.ks);
-  p.hpw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0 ? 2 : 1);
+  p.hpw = query_heads_per_wg(p.group);
   p.rbw = 4 / p.hpw;
-  const int64_t rows_per_wg = (int64_t)p.rbw * rows_per_wave;
+  const int64_t rows_per_wg = query_rows_per_wg(p.group, rows_per_wave);
   p.n_row_groups = (int32_t)((sq + rows_per_wg - 1) / rows_per_wg);
   p.n_head_groups = a->hq / p.hpw;
   const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
@@ -628,6 +635,24 @@ int bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
 }  // namespace
 
 extern "C" {
+
+int rba_step_full_tiles(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t sk, const rba_segs* kv_segs,
+                        int32_t* fwd_full, int32_t* bwd_full) {
+  g_err.clear();
+  if (!fwd_full || !bwd_full) return fail(RBA_ERR_INVALID, "fwd_full / bwd_full is NULL");
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
+  if (rc) return rc;
+  // the row groups of the forward and dQ launches (fill_query_tiling) and
+  // the key tiles of the dK/dV launch (bwd_step)
+  const int group = a->hq / a->hkv;
+  const int64_t fwd_rows = query_rows_per_wg(group, rba::fwd_rows_per_wave(a->d, a->dtype == RBA_BF16));
+  const int64_t dq_rows = query_rows_per_wg(group, 32);
+  *fwd_full = all_tiles_full(a, plan, sq, sk, fwd_rows) ? 1 : 0;
+  *bwd_full = (all_tiles_full(a, plan, sq, sk, dq_rows) && all_blocks_full(a, plan, sq, sk, rba::bwd_keys_per_wg(a->d)))
+                  ? 1 : 0;
+  return RBA_OK;
+}
 
 int rba_bwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
                  int64_t sk, const rba_segs* kv_segs, const void* d_o, const float* lse, const float* delta,

@@ -27,7 +27,7 @@ RBA_MAX_SEGS = 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
 EXPORTS = ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-           "rba_plan_step", "rba_last_error", "rba_version")
+           "rba_plan_step", "rba_step_full_tiles", "rba_last_error", "rba_version")
 
 
 class RbaError(RuntimeError):
@@ -97,8 +97,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rba_bwd_step.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_bwd_step_acc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
+    lib.rba_step_full_tiles.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     for fn in ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-               "rba_plan_step"):
+               "rba_plan_step", "rba_step_full_tiles"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
     lib.rba_last_error.argtypes = []
@@ -201,6 +202,14 @@ def rba_plan_step(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs: rba_
     rc = _check("rba_plan_step", load().rba_plan_step(
         ctypes.byref(a), sq, ctypes.byref(q_segs), sk, ctypes.byref(kv_segs), ctypes.byref(pairs)))
     return rc, pairs.value
+
+
+def rba_step_full_tiles(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs: rba_segs) -> Tuple[int, int]:
+    """(forward full, backward full) launch choices of a step — host only, no device needed."""
+    f, b = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("rba_step_full_tiles", load().rba_step_full_tiles(
+        ctypes.byref(a), sq, ctypes.byref(q_segs), sk, ctypes.byref(kv_segs), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
 
 
 def rba_version() -> str:
