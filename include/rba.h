@@ -243,7 +243,8 @@ int rba_plan_step(const rba_attn* a, int64_t sq, const rba_segs* q_segs,
  * every query block a workgroup of keys visits is allowed for all of its
  * keys.  These are launch choices of this library (the results are the same
  * either way); the call exists so that the decision can be checked against
- * an enumeration of the visited tiles.  The document mask always gives 0.
+ * an enumeration of the visited tiles.  The document mask and fp32 steps
+ * (whose kernels always classify tiles) give 0.
  * Returns RBA_OK, or an error for invalid arguments (as rba_plan_step).
  */
 int rba_step_full_tiles(const rba_attn* a, int64_t sq, const rba_segs* q_segs,

@@ -646,10 +646,13 @@ int rba_step_full_tiles(const rba_attn* a, int64_t sq, const rba_segs* q_segs, i
   // the row groups of the forward and dQ launches (fill_query_tiling) and
   // the key tiles of the dK/dV launch (bwd_step)
   const int group = a->hq / a->hkv;
-  const int64_t fwd_rows = query_rows_per_wg(group, rba::fwd_rows_per_wave(a->d, a->dtype == RBA_BF16));
+  const int64_t fwd_rows = query_rows_per_wg(group, rba::fwd_rows_per_wave(a->d, 1));
   const int64_t dq_rows = query_rows_per_wg(group, 32);
-  *fwd_full = all_tiles_full(a, plan, sq, sk, fwd_rows) ? 1 : 0;
-  *bwd_full = (all_tiles_full(a, plan, sq, sk, dq_rows) && all_blocks_full(a, plan, sq, sk, rba::bwd_keys_per_wg(a->d)))
+  // only the bf16 kernels have mask-free instantiations (the backward is bf16 only)
+  const bool bf16 = a->dtype == RBA_BF16;
+  *fwd_full = (bf16 && all_tiles_full(a, plan, sq, sk, fwd_rows)) ? 1 : 0;
+  *bwd_full = (bf16 && all_tiles_full(a, plan, sq, sk, dq_rows) &&
+               all_blocks_full(a, plan, sq, sk, rba::bwd_keys_per_wg(a->d)))
                   ? 1 : 0;
   return RBA_OK;
 }

@@ -126,6 +126,14 @@ def test_document_mask_never_full():
     assert (ff, bf) == (0, 0)
 
 
+def test_fp32_steps_never_full():
+    a = rba.attn_params(4, 4, 64, 0.125, rba.RBA_F32, rba.RBA_MASK_CAUSAL)
+    ff, bf = rba.rba_step_full_tiles(a, 128, rba.make_segs([(4096, 128)]), 128, rba.make_segs([(0, 128)]))
+    assert (ff, bf) == (0, 0)
+    a.dtype = rba.RBA_BF16   # the same step in bf16 takes the mask-free kernels
+    assert rba.rba_step_full_tiles(a, 128, rba.make_segs([(4096, 128)]), 128, rba.make_segs([(0, 128)])) == (1, 1)
+
+
 @pytest.mark.parametrize("rank", [0, 3, 7])
 def test_zigzag_ring_steps_take_the_full_path(rank):
     """32K causal zigzag over 8 ranks: every step but the rank's own chunk is full."""
