@@ -152,8 +152,9 @@ struct KvLoader {
     sk = p.sk;
     r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;
     loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
-    // the swizzle step only touches the chunk bits, below the row stride
-    // (a multiple of 256 bytes), so the row step adds independently
+    // load i's row step moves from the scalar base into its lane offset
+    // (the same address); the offset stays below 64 rows of K or V, so
+    // under the 4 GiB the host allows for a tensor, and cannot wrap
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       loffs[i] = (loff0 ^ ((uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4)) + (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
