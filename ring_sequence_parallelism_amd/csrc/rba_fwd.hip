@@ -29,6 +29,9 @@
 //     arithmetic) or partial (per-element mask; a tile wholly masked for
 //     one wave but needed by another is computed masked, so the tile body
 //     has no branch around it).
+//     Steps whose visited tiles the host has shown to be all full run an
+//     instantiation with no classification and no mask code.
+//   * Scheduling groups keep 6 K reads in flight ahead of the score MFMAs.
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score,
 //     and a lazy running maximum that rarely rescales O.
 #include <type_traits>
