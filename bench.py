@@ -14,11 +14,13 @@ d = 128, bf16, inputs N(0,1) plus a seeded dO.
 
 value = effective FLOPs of the step (4*d per allowed (query, key, head)
 triple in the forward, 10*d in the backward; masked and skipped work is not
-counted) / time of the step, with all inputs resident in HBM.
+counted) / time of the step, with all inputs resident in HBM.  The
+breakdown also reports the forward replay of one rank of a 524288-token
+causal zigzag split (8 steps of 65536 keys; --no-long-forward skips it).
 
 Prints ONE JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--extra] [--flush-mib 512]
+                    [--no-long-forward] [--extra] [--flush-mib 512]
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true",
                     help="also time the forward replays of the 64K packed-document and 512K zigzag workloads")
+    ap.add_argument("--no-long-forward", action="store_true",
+                    help="skip the 512K zigzag forward replay reported in the breakdown")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows in the CPU-oracle sample")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
@@ -157,6 +161,28 @@ def cpu_baseline(w, rows_n):
                       f"{w.rank} (all {w.hq} heads) against all {w.seq} keys; {secs:.1f} s on "
                       f"{cores} visible host cores, BLAS threads {blas_threads}; effective flops "
                       f"counted as on the GPU (14*d per allowed pair and head)"}
+
+
+def forward_replay_rate(torch, RingReplay, wx, ranks, reps=2):
+    """Effective forward TFLOP/s of the ring replays of `ranks` (sum of the
+    rba_fwd_step / rba_fwd_step_acc launch times, events on the launch stream)."""
+    fl, ms_tot = 0, 0.0
+    for r in ranks:
+        rx = RingReplay(wx, r, "cuda")
+        rx.forward()
+        torch.cuda.synchronize()
+        tm = LaunchTimer(torch)
+        for _ in range(reps):
+            rx.forward(on_step=tm)
+        tm.close()
+        torch.cuda.synchronize()
+        ms_tot += sum(ms for kind, _, ms in tm.durations() if kind == "fwd") / reps
+        fl += rx.fwd_flops()
+        del rx
+        torch.cuda.empty_cache()
+    t = fl / (ms_tot * 1e-3) / 1e12
+    return {"fwd_step_tflops": round(t, 2), "frac_peak": round(t / PEAK_BF16_TFLOPS, 4),
+            "fwd_ms": round(ms_tot, 3), "ranks": len(ranks)}
 
 
 def main():
@@ -313,27 +339,13 @@ def main():
                            "fwd_ms": round(f_ms, 3)}
         del sx
         torch.cuda.empty_cache()
-        for key in ("c3", "c4"):
-            wx = W.WORKLOADS[key]
-            ranks = range(wx.n_ranks) if key == "c3" else [wx.rank]
-            fl, ms_tot = 0, 0.0
-            for r in ranks:
-                rx = RingReplay(wx, r, "cuda")
-                rx.forward()
-                torch.cuda.synchronize()
-                reps = 2
-                tm = LaunchTimer(torch)
-                for _ in range(reps):
-                    rx.forward(on_step=tm)
-                tm.close()
-                torch.cuda.synchronize()
-                ms_tot += sum(ms for kind, _, ms in tm.durations() if kind == "fwd") / reps
-                fl += rx.fwd_flops()
-                del rx
-            t = fl / (ms_tot * 1e-3) / 1e12
-            extra[wx.name] = {"fwd_step_tflops": round(t, 2), "frac_peak": round(t / PEAK_BF16_TFLOPS, 4),
-                              "fwd_ms": round(ms_tot, 3), "ranks": len(ranks)}
-            torch.cuda.empty_cache()
+        wx = W.WORKLOADS["c3"]
+        extra[wx.name] = forward_replay_rate(torch, RingReplay, wx, range(wx.n_ranks))
+    # The 512K causal zigzag forward (one rank's 8 steps of 65536 keys) is the
+    # long-sequence forward figure; it is reported on every run (about 10 s).
+    if not args.no_long_forward:
+        wx = W.WORKLOADS["c4"]
+        breakdown["fwd_512k_zigzag"] = forward_replay_rate(torch, RingReplay, wx, [wx.rank])
 
     cpu = None
     if not args.no_cpu_baseline:
