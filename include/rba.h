@@ -118,7 +118,7 @@ typedef struct {
  * Returns RBA_OK, RBA_STEP_EMPTY (host-side proof that no pair is allowed:
  * nothing launched, outputs untouched — the caller skips the merge), or an
  * error.  sq = 0 or sk = 0 is RBA_STEP_EMPTY.
- * dtype RBA_BF16 supports d in {64, 128}; RBA_F32 supports d = 64.
+ * dtype RBA_BF16 and RBA_F32 both support d in {64, 128}.
  */
 int rba_fwd_step(const rba_attn* a,
                  const void* q, int64_t sq, const rba_segs* q_segs,
@@ -150,6 +150,11 @@ int rba_fwd_step_acc(const rba_attn* a,
 
 /*
  * rba_merge — LSE-weighted merge of a step's partial into the running result.
+ * Defining passage: the blockwise exact attention the TASP page builds on
+ * (FlashAttention and "Self-attention Does Not Need O(n^2) Memory", both in
+ * the "Builds on" list of its citation map): softmax attention over a union
+ * of disjoint key sets equals the partial results over each set combined
+ * with weights exp(LSE_part - LSE_total); with two sets,
  *   L = ln(e^{lse_acc} + e^{lse_part}),
  *   o_acc = e^{lse_acc - L} o_acc + e^{lse_part - L} o_part,  lse_acc = L.
  *   A side with LSE = -inf has weight 0; both -inf gives (0, -inf).
@@ -159,14 +164,31 @@ int rba_fwd_step_acc(const rba_attn* a,
  *   o_final (nullable): also write the merged O as final_dtype (RBA_BF16 rounds
  *   to nearest even, RBA_F32 copies) into o_final [sq, hq, d].
  *   o_acc may not alias o_part; o_final may not alias either.
- * d must be a multiple of 4 and at most 1024.
+ * d must be a multiple of 4 in [4, 1024], else RBA_ERR_UNSUPPORTED.  Every
+ * (row, head) pair is merged by threads of a single wave (rba_merge_layout),
+ * so the in-place update of lse_acc never races with a read of it.
  */
 int rba_merge(int64_t sq, int32_t hq, int32_t d,
               float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
               void* o_final, int32_t final_dtype, void* stream);
 
 /*
+ * rba_merge_layout — host-only (no device access): the thread map rba_merge
+ * launches for head dimension d.  A workgroup has *threads_per_wg threads;
+ * thread t works on (row, head) pair slot t / *lanes_per_pair of the
+ * workgroup's sweep and on the 16-byte vectors (t % lpp) + i * lpp,
+ * i < *vecs_per_lane, of that pair (lpp = *lanes_per_pair, a power of two
+ * dividing 64, so one pair's threads are lanes of one 64-lane wave).
+ * Returns RBA_OK, or RBA_ERR_UNSUPPORTED for a d that rba_merge rejects.
+ */
+int rba_merge_layout(int32_t d, int32_t* lanes_per_pair, int32_t* vecs_per_lane, int32_t* threads_per_wg);
+
+/*
  * rba_bwd_preprocess — delta[h, i] = sum_c dO[i, h, c] * O[i, h, c], fp32.
+ * Defining passage: the backward of the attention definition above; the
+ * pages' workload is training (HSAP page, "Methodology" and "Key Results":
+ * training throughput on packed long sequences), whose backward pass needs,
+ * per query row, this inner product of the output and its gradient.
  *   o [sq, hq, d] in o_dtype (the forward's merged output: the fp32
  *   accumulator gives delta without the output's bf16 rounding), d_o
  *   [sq, hq, d] in do_dtype (its upstream gradient); delta [hq, sq] fp32.
@@ -177,7 +199,11 @@ int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32
 
 /*
  * rba_bwd_step — one ring step of the backward pass (the gradient of
- * L = sum dO * O through this step's keys).  With P_ij = exp(s_ij - lse_i)
+ * L = sum dO * O through this step's keys).  Defining passage: the
+ * derivative of the attention definition at the top of this header, taken
+ * step by step over the ring as in the forward (TASP abstract: each query
+ * chunk meets every KV chunk); training is the pages' workload (HSAP page,
+ * "Methodology" and "Key Results").  With P_ij = exp(s_ij - lse_i)
  * for allowed pairs (lse = the FINAL merged LSE of the forward) and
  * dS_ij = P_ij (<dO_i, v_j> - delta_i):
  *   dq_acc[i] += scale * sum_j dS_ij k_j            (accumulated, in/out)

@@ -492,7 +492,20 @@ int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, c
   p.o_acc = o_acc; p.lse_acc = lse_acc; p.o_part = o_part; p.lse_part = lse_part;
   p.o_final = o_final; p.final_bf16 = final_dtype == RBA_BF16;
   p.n_pairs = sq * hq; p.sq = (int32_t)sq; p.hq = hq; p.d = d;
+  rba::merge_lanes(d, &p.lanes_per_pair, &p.vecs_per_lane);
   return hip_status(rba::launch_merge(p, (hipStream_t)stream), "merge");
+}
+
+int rba_merge_layout(int32_t d, int32_t* lanes_per_pair, int32_t* vecs_per_lane, int32_t* threads_per_wg) {
+  g_err.clear();
+  if (!lanes_per_pair || !vecs_per_lane || !threads_per_wg) return fail(RBA_ERR_INVALID, "output pointer is NULL");
+  if (d < 4 || d > 1024 || d % 4) return fail(RBA_ERR_UNSUPPORTED, "merge: d = %d (multiple of 4, <= 1024)", d);
+  int lpp = 0, vpl = 0;
+  rba::merge_lanes(d, &lpp, &vpl);
+  *lanes_per_pair = lpp;
+  *vecs_per_lane = vpl;
+  *threads_per_wg = rba::kMergeThreads;
+  return RBA_OK;
 }
 
 int rba_bwd_preprocess(int64_t sq, int32_t hq, int32_t d, int32_t o_dtype, int32_t do_dtype, const void* o,

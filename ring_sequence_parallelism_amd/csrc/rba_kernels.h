@@ -9,8 +9,9 @@
 namespace rba {
 
 constexpr int kMaxSegs = 16;
-constexpr int kMaxOrder = 512;
-constexpr int kFwdTileKeys = 64;   // keys per tile of the query-stationary kernels   // longest host-computed workgroup order passed in kernel arguments
+constexpr int kMaxOrder = 512;   // longest host-computed workgroup order passed in kernel arguments
+constexpr int kFwdTileKeys = 64;   // keys per tile of the query-stationary kernels
+constexpr int kMergeThreads = 256;  // threads per workgroup of the merge and preprocess kernels
 
 // A chunk's rows mapped to global positions: rows [row0[s], row0[s+1]) hold
 // positions start[s], start[s] + stride[s], ...  (row0[n] = number of rows).
@@ -101,7 +102,21 @@ struct MergeParams {
   int32_t final_bf16;    // 1: o_final is bf16, 0: fp32
   int64_t n_pairs;       // sq * hq
   int32_t sq, hq, d;
+  // thread map (merge_lanes): a pair's lanes_per_pair consecutive threads
+  // (a power of two dividing 64) each move vecs_per_lane 16-byte vectors
+  int32_t lanes_per_pair, vecs_per_lane;
 };
+
+// Thread map of the merge kernel for head dimension d (a multiple of 4 in
+// [4, 1024]): lanes per pair = the smallest power of two >= d / 4, at most
+// 64; vectors per lane = ceil(d / 4 / lanes per pair).
+inline void merge_lanes(int d, int* lanes_per_pair, int* vecs_per_lane) {
+  const int nv = d / 4;
+  int lpp = 1;
+  while (lpp < nv && lpp < 64) lpp *= 2;
+  *lanes_per_pair = lpp;
+  *vecs_per_lane = (nv + lpp - 1) / lpp;
+}
 
 struct PrepParams {
   const void* o;

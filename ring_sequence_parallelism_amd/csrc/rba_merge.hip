@@ -6,42 +6,51 @@
 //   O = e^{La - L} Oa + e^{Lb - L} Ob,  LSE = L,
 // and a side with LSE = -inf carrying weight 0.
 //
-// Both kernels stream memory once; they are bound by HBM bandwidth.  A
-// (row, head) pair is handled by d/4 consecutive threads, each moving one
-// 16-byte vector of every operand, so every wave reads and writes whole
-// contiguous rows.  The two LSE values of a pair are read by all its threads
-// from the same address (one request).
+// Both kernels stream memory once; they are bound by HBM bandwidth.
+//
+// Merge thread map.  A (row, head) pair of d / 4 16-byte vectors is handled
+// by a group of `lpp` consecutive threads, lpp = the smallest power of two
+// >= d / 4, capped at 64 (merge_lanes in the host layer); thread t of a
+// workgroup takes pair slot t / lpp and vectors (t % lpp) + i * lpp for
+// i < vpl = ceil(d / 4 / lpp).  Since lpp divides 64, a pair's threads are
+// lanes of one wave: they all read the pair's two LSE values before the
+// wave's single store of the merged LSE (program order within a wave, and
+// the stored value depends on the loaded ones), so no thread of the pair
+// can read an LSE that is already merged, whatever d is.
 #include "rba_device.h"
 
 namespace rba {
 
-constexpr int kMergeThreads = 256;
-
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
-  const int tpp = p.d >> 2;                       // threads per (row, head) pair
-  const int ppb = kMergeThreads / tpp;            // pairs per block per sweep
-  const int sub = threadIdx.x / tpp, c4 = threadIdx.x % tpp;
-  if (sub >= ppb) return;
+  const int lpp = p.lanes_per_pair, vpl = p.vecs_per_lane;
+  const int ppb = kMergeThreads / lpp;            // pairs per block per sweep
+  const int sub = threadIdx.x / lpp, c0 = threadIdx.x % lpp;
+  const int nv = p.d >> 2;                        // 16-byte vectors per pair
   for (int64_t pair = (int64_t)blockIdx.x * ppb + sub; pair < p.n_pairs; pair += (int64_t)gridDim.x * ppb) {
     const int row = (int)(pair / p.hq), h = (int)(pair % p.hq);
     const size_t li = (size_t)h * p.sq + row;
-    const size_t oi = (size_t)pair * p.d + 4 * c4;
-    f32x4 o = *reinterpret_cast<const f32x4*>(p.o_acc + oi);
-    if (p.o_part) {
-      const MergeWeights w = merge_weights(p.lse_acc[li], p.lse_part[li]);
-      const f32x4 ob = *reinterpret_cast<const f32x4*>(p.o_part + oi);
-      o = w.wa * o + w.wb * ob;
-      *reinterpret_cast<f32x4*>(p.o_acc + oi) = o;
-      if (c4 == 0) p.lse_acc[li] = w.L;
-    }
-    if (p.o_final) {
-      if (p.final_bf16) {
-        u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi) = w;
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi) = o;
+    MergeWeights w{1.f, 0.f, 0.f};
+    if (p.o_part) w = merge_weights(p.lse_acc[li], p.lse_part[li]);
+    for (int i = 0; i < vpl; ++i) {
+      const int c4 = c0 + i * lpp;
+      if (c4 >= nv) break;
+      const size_t oi = (size_t)pair * p.d + 4 * c4;
+      f32x4 o = *reinterpret_cast<const f32x4*>(p.o_acc + oi);
+      if (p.o_part) {
+        const f32x4 ob = *reinterpret_cast<const f32x4*>(p.o_part + oi);
+        o = w.wa * o + w.wb * ob;
+        *reinterpret_cast<f32x4*>(p.o_acc + oi) = o;
+      }
+      if (p.o_final) {
+        if (p.final_bf16) {
+          u32x2 b = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi) = b;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi) = o;
+        }
       }
     }
+    if (p.o_part && c0 == 0) p.lse_acc[li] = w.L;
   }
 }
 
@@ -85,7 +94,7 @@ static int grid_for(int64_t n_pairs, int ppb) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
-  const int ppb = kMergeThreads / (p.d >> 2);
+  const int ppb = kMergeThreads / p.lanes_per_pair;
   hipLaunchKernelGGL(merge_kernel, dim3(grid_for(p.n_pairs, ppb)), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }

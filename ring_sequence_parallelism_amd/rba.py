@@ -27,7 +27,7 @@ RBA_MAX_SEGS = 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
 EXPORTS = ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-           "rba_plan_step", "rba_step_full_tiles", "rba_last_error", "rba_version")
+           "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_last_error", "rba_version")
 
 
 class RbaError(RuntimeError):
@@ -98,8 +98,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rba_bwd_step_acc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, P, P, P, P, P]
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
     lib.rba_step_full_tiles.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    lib.rba_merge_layout.argtypes = [I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
     for fn in ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-               "rba_plan_step", "rba_step_full_tiles"):
+               "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
     lib.rba_last_error.argtypes = []
@@ -210,6 +211,15 @@ def rba_step_full_tiles(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs
     _check("rba_step_full_tiles", load().rba_step_full_tiles(
         ctypes.byref(a), sq, ctypes.byref(q_segs), sk, ctypes.byref(kv_segs), ctypes.byref(f), ctypes.byref(b)))
     return f.value, b.value
+
+
+def rba_merge_layout(d: int) -> Tuple[int, int, int, int]:
+    """(status, lanes per pair, vectors per lane, threads per workgroup) of
+    rba_merge's thread map for head dimension d — host only.  The status is
+    returned, not raised, so that rejected d can be checked."""
+    lpp, vpl, tpw = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load().rba_merge_layout(int(d), ctypes.byref(lpp), ctypes.byref(vpl), ctypes.byref(tpw))
+    return rc, lpp.value, vpl.value, tpw.value
 
 
 def rba_version() -> str:

@@ -310,3 +310,36 @@ def test_strided_overlap_matches_brute_force(seed):
         share = len(set(pos.tolist())) < pos.size
         rc = _plan_rc(a, segs)
         assert (rc == rba.RBA_ERR_INVALID) == share, segs
+
+
+def test_merge_thread_map_keeps_each_pair_in_one_wave():
+    """For every d rba_merge accepts, the thread map it launches puts all
+    threads of a (row, head) pair in one 64-lane wave (the pair's LSE is read
+    by all of them and then overwritten in place by one of them), and covers
+    each of the pair's d / 4 vectors exactly once.  Every other d is refused
+    by both the layout query and rba_merge itself."""
+    lib = rba.load()
+    for d in range(-8, 1100):
+        rc, lpp, vpl, tpw = rba.rba_merge_layout(d)
+        accepted = d >= 4 and d <= 1024 and d % 4 == 0
+        if not accepted:
+            assert rc == rba.RBA_ERR_UNSUPPORTED, d
+            assert lib.rba_merge(8, 2, d, FAKE, FAKE, FAKE, FAKE, None, 0, None) == rba.RBA_ERR_UNSUPPORTED, d
+            continue
+        assert rc == rba.RBA_OK, d
+        nv = d // 4
+        assert tpw % 64 == 0 and tpw % lpp == 0, (d, lpp, tpw)
+        covered = {}
+        for t in range(tpw):
+            slot, c0 = t // lpp, t % lpp
+            covered.setdefault(slot, []).append(t // 64)
+            for i in range(vpl):
+                c = c0 + i * lpp
+                if c < nv:
+                    covered.setdefault(("vec", slot), []).append(c)
+        for slot in range(tpw // lpp):
+            waves = set(covered[slot])
+            assert len(waves) == 1, f"d={d}: pair slot {slot} spans waves {sorted(waves)}"
+            vecs = sorted(covered[("vec", slot)])
+            assert vecs == list(range(nv)), f"d={d}: pair slot {slot} vectors {vecs[:8]}..."
+

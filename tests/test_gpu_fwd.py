@@ -150,8 +150,8 @@ def _run_scaled_keys(sq, sk, hq, hkv, d, mask, qsegs, ksegs, row_scale, seed):
 def test_step_score_range(pattern, mask):
     # Key norms that change along the chunk move the row maximum by far more
     # than 2^16 between key tiles (jump, ramp) or leave later tiles far below
-    # it (drop): exercises the running reference, its rescale and the redo of
-    # a tile whose exponentials would leave the accepted range.
+    # it (drop): exercises the lazy running maximum (moved only when a tile's
+    # maximum exceeds it by more than 2^8) and the rescale of O and l.
     sq, sk, hq, hkv, d = 96, 448, 4, 2, 128
     _say("fwd score range", pattern, "mask", mask)
     rows = np.arange(sk)
@@ -190,8 +190,10 @@ def test_step_deterministic():
 # ---------------------------------------------------------------------------
 # merge
 
-@pytest.mark.parametrize("d", [64, 128, 36])
+@pytest.mark.parametrize("d", [4, 36, 64, 128, 260, 1024])
 def test_merge_kernel(d):
+    # d = 36 and 260: pairs of 9 and 65 vectors, whose threads the merge's
+    # thread map still keeps inside one wave (16 and 64 lanes per pair)
     _say("merge d", d)
     rng = np.random.default_rng(d)
     sq, hq = 333, 5
