@@ -122,7 +122,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
   constexpr int QT = kBQ * RB;               // bytes of a Q or dO block tile
-  constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
+  using A = DkdvAddr<D, kBK, kBQ, 4>;        // lane addresses of the tile loads
   // K tile (once), double-buffered Q / dO tiles and LSE / delta rows (loaded
   // straight from HBM into LDS).
   char* k_lds = smem;
@@ -170,13 +170,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // K tile rows [kr0, kr0 + 128) (rows past the chunk re-read its last row).
   if (first.valid) {
 #pragma unroll
-    for (int i = 0; i < kBK / ROWS_PER_LOAD / 4; ++i) {
-      const int ld = wave * (kBK / ROWS_PER_LOAD / 4) + i;
-      const int r = ld * ROWS_PER_LOAD + lane / CPR;
-      const int c = (lane % CPR) ^ tile_swz<CPR>(r);
-      const uint32_t krow = (uint32_t)min(kr0 + r, p.sk - 1);
-      dma16(kg, krow * k_row_bytes + (uint32_t)(c << 4), lds_addr(k_lds) + ld * 1024);
-    }
+    for (int i = 0; i < A::KLOADS; ++i)
+      dma16(kg, A::k_off(kr0, wave, i, lane, p.sk, k_row_bytes), lds_addr(k_lds) + (wave * A::KLOADS + i) * 1024);
   }
 
   // V rows as B operands of dP = dO V^T (lane: key col, d = 16*ks + 8*half + 0..7).
@@ -207,13 +202,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // (rows past the end re-read the last row and are masked) and, from wave
   // 0, the block's LSE and delta rows.  The per-lane
   // byte offsets inside a full block are loop invariant.
-  constexpr int QLOADS = kBQ / ROWS_PER_LOAD / 4;
+  constexpr int QLOADS = A::QLOADS;
   uint32_t qoff[QLOADS];
 #pragma unroll
-  for (int i = 0; i < QLOADS; ++i) {
-    const int r = (wave * QLOADS + i) * ROWS_PER_LOAD + lane / CPR;
-    qoff[i] = (uint32_t)r * q_row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
-  }
+  for (int i = 0; i < QLOADS; ++i) qoff[i] = A::q_whole_off(wave, i, lane, q_row_bytes);
   const uint32_t qd_wave = lds_addr(&qd_lds[0][0][0]) + wave * QLOADS * 1024;
   const float* lse_h = nullptr;
   const float* dlt_h = nullptr;
@@ -221,7 +213,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     const int qr0 = b.qbk * kBQ;
     const uint32_t dst = qd_wave + buf * 2 * QT;
     if (qr0 + kBQ <= p.sq) {
-      const size_t bb = (size_t)qr0 * q_row_bytes;
+      const size_t bb = A::block_base(qr0, q_row_bytes);
 #pragma unroll
       for (int i = 0; i < QLOADS; ++i) {
         dma16(qg + bb, qoff[i], dst + i * 1024);
@@ -230,16 +222,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     } else {
 #pragma unroll
       for (int i = 0; i < QLOADS; ++i) {
-        const int r = (wave * QLOADS + i) * ROWS_PER_LOAD + lane / CPR;
-        const uint32_t off = (uint32_t)min(qr0 + r, p.sq - 1) * q_row_bytes +
-                             (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r)) << 4);
+        const uint32_t off = A::q_ragged_off(qr0, wave, i, lane, p.sq, q_row_bytes);
         dma16(qg, off, dst + i * 1024);
         dma16(dog, off, dst + QT + i * 1024);
       }
     }
     if (wave == 0) {
       // lanes l and l + 32 both fetch row qr0 + l (rows past the end: the last row)
-      const uint32_t off = 4u * (uint32_t)min(qr0 + col, p.sq - 1);
+      const uint32_t off = A::lse_off(qr0, lane, p.sq);
       dma4(lse_h, off, lds_addr(ld_lds[buf][0]));
       dma4(dlt_h, off, lds_addr(ld_lds[buf][1]));
     }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rba_addr.h"
 #include "rba_kernels.h"
 
 namespace rba {
@@ -181,26 +182,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int stride, i
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// XOR swizzle of 16-byte chunks inside a row of a bf16 tile that has no
-// padding (rows of CPR chunks, CPR = 16 for d = 128, 8 for d = 64): chunk c of
-// row r is stored at chunk position c ^ tile_swz(r).  The map is linear over
-// GF(2) in the row bits (tile_swz(a ^ b) = tile_swz(a) ^ tile_swz(b)).  For
-// CPR = 16 (bit k of the result from row bits: 0 <- 2, 1 <- 1, 2 <- 0,
-// 3 <- 1 ^ 3):
-//   * 16-byte row reads (one chunk of 16 consecutive rows per 16 lanes, 8 per
-//     8) land on 16 (8) distinct chunk positions modulo 16 (8);
-//   * transpose reads (4 consecutive rows, 2 or 4 consecutive chunks from an
-//     aligned pair / quad) land on distinct positions modulo 8 / 16,
-// so neither access pattern has a bank conflict with 32 or with 64 banks of
-// 4 bytes.  CPR = 8 keeps the analogous (2 * (r & 3)) | ((r >> 2) & 1).
-template <int CPR>
-__device__ __forceinline__ int tile_swz(int r) {
-  if (CPR == 16) {
-    const int b1 = (r >> 1) & 1;
-    return ((r >> 2) & 1) | (b1 << 1) | ((r & 1) << 2) | ((b1 ^ ((r >> 3) & 1)) << 3);
-  }
-  return (2 * (r & 3)) | ((r >> 2) & 1);
-}
+// tile_swz (the XOR swizzle of 16-byte chunks in a tile row) is in rba_addr.h.
 
 // tr_operand for a swizzled, unpadded tile (base = byte address of row 0).
 template <int CPR>

@@ -118,24 +118,16 @@ __device__ __forceinline__ PosRange tile_pos_range(const TileIter& it, const Seg
 
 // Direct-to-LDS loads of K and V key tiles (kBN rows of one KV head) into
 // double-buffered LDS tiles of unpadded, swizzled rows: [buffer][K, V][tile].
-// Load i of a wave fills tile rows (wave * LOADS + i) * ROWS_PER_LOAD +
-// lane / CPR: lane l writes chunk position l % CPR of its row and fetches the
-// global chunk that the swizzle stores there.  Load i covers rows r_lane +
-// ROWS_PER_LOAD * i, where the two terms share no set bit (r_lane = 16 * wave
-// + lane / 16 for d = 128, 16 * wave + lane / 8 for d = 64), so its row term
-// is a uniform step of load 0's and, tile_swz being XOR-linear, its swizzled
-// chunk is load 0's XOR tile_swz(ROWS_PER_LOAD * i): the per-lane offsets are
-// one loop-invariant register and a tile adds a uniform base.  In the last,
-// ragged tile, lanes whose row is past the end of the chunk step back to its
-// last row (finite values, masked out).
+// The lane addresses (which row and chunk each lane fetches, and the clamp
+// of the last, ragged tile to the chunk's last row) are KvTileAddr's; the
+// per-lane offsets of a whole tile are loop invariant and a tile adds a
+// uniform base.
 template <int D>
 struct KvLoader {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  using A = KvTileAddr<D, kBN, kWaves>;
   static constexpr int RB = D * 2;                  // bytes per tile row
   static constexpr int TILE = kBN * RB;             // bytes per K or V tile
-  static constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide 16-byte load covers
-  static constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;   // per wave per tensor per tile
-  static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile rows");
+  static constexpr int LOADS = A::LOADS;            // per wave per tensor per tile
 
   const char* kg;       // K and V rows of the KV head (uniform)
   const char* vg;
@@ -150,40 +142,25 @@ struct KvLoader {
     kg = uniform_ptr(static_cast<const char*>(p.k) + (uint32_t)(g * RB));
     vg = uniform_ptr(static_cast<const char*>(p.v) + (uint32_t)(g * RB));
     sk = p.sk;
-    r_lane = wave * LOADS * ROWS_PER_LOAD + lane / CPR;
-    loff0 = (uint32_t)r_lane * row_bytes + (uint32_t)(((lane % CPR) ^ tile_swz<CPR>(r_lane)) << 4);
-    // load i's row step moves from the scalar base into its lane offset
-    // (the same address); the offset stays below 64 rows of K or V, so
-    // under the 4 GiB the host allows for a tensor, and cannot wrap
+    r_lane = A::r_lane(wave, lane);
+    loff0 = A::loff0(wave, lane, row_bytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      loffs[i] = (loff0 ^ ((uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4)) + (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
+    for (int i = 0; i < LOADS; ++i) loffs[i] = A::whole_off(loff0, i, row_bytes);
     lds_wave = lds_base + wave * LOADS * 1024;
   }
 
   // Loads key tile kt into buffer b.
   __device__ __forceinline__ void issue(int kt, int b) const {
     const uint32_t dst = lds_wave + b * 2 * TILE;
-    const bool whole = (kt + 1) * kBN <= sk;
-    if (whole) {
+    const size_t tb = A::tile_base(kt, row_bytes);
+    if ((kt + 1) * kBN <= sk) {
       // one scalar base per tensor; the row steps are in the lane offsets
-      const size_t tb = (size_t)kt * kBN * row_bytes;
       dma16_kv<LOADS>(kg + tb, vg + tb, loffs, dst, dst + TILE);
       return;
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      size_t tb = ((size_t)kt * kBN + i * ROWS_PER_LOAD) * row_bytes;
-      uint32_t off = loff0 ^ ((uint32_t)tile_swz<CPR>(ROWS_PER_LOAD * i) << 4);
-      if (!whole) {
-        // Relative to the tile's first row: the clamped row is at or past
-        // it, so the unsigned lane offset never wraps (load i's own first
-        // row may lie past the end of the chunk).
-        tb = (size_t)kt * kBN * row_bytes;
-        off += (uint32_t)(i * ROWS_PER_LOAD) * row_bytes;
-        const int over = kt * kBN + r_lane + i * ROWS_PER_LOAD - (sk - 1);
-        if (over > 0) off -= (uint32_t)over * row_bytes;
-      }
+      const uint32_t off = A::ragged_off(kt, i, r_lane, loff0, row_bytes, sk);
       dma16(kg + tb, off, dst + i * 1024);
       dma16(vg + tb, off, dst + TILE + i * 1024);
     }
