@@ -48,17 +48,23 @@ class RingReplay:
     """Device-resident inputs and buffers of one rank's ring replay."""
 
     def __init__(self, w: W.Workload, rank: Optional[int] = None, device="cuda",
-                 kv_sources: Optional[List[int]] = None, with_grad: bool = False):
+                 kv_sources: Optional[List[int]] = None, with_grad: bool = False,
+                 order: Optional[List[int]] = None, kv: Optional[Dict[str, Dict[int, torch.Tensor]]] = None):
+        """``order``: the KV chunks of the steps in replay order (default: ring
+        order; a caller may permute, drop or repeat chunks).  ``kv``: device
+        K / V chunks already made for this workload ({"k": {j: tensor},
+        "v": {j: tensor}}), shared instead of generated again."""
         self.w = w
         self.r = w.rank if rank is None else rank
         self.device = torch.device(device)
         self.dtype = rba.RBA_BF16 if w.dtype == "bf16" else rba.RBA_F32
         n = w.n_ranks
-        self.order = ring_order(self.r, n)
+        self.order = ring_order(self.r, n) if order is None else list(order)
         srcs = sorted(set(self.order if kv_sources is None else kv_sources))
         # inputs
         self.q = to_device(W.gen_rank_chunk(w, W.T_Q, self.r), w.dtype, self.device)
         self.q_segs = rba.make_segs(w.rank_runs(self.r))
+        self._shared_kv = kv
         self.order = self._build_kv(srcs)
         self.cu_host = None
         self.cu_dev = None
@@ -96,8 +102,11 @@ class RingReplay:
         """Device K / V and segments of every step, keyed as the steps are;
         returns the step keys in replay order."""
         w = self.w
-        self.k = {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, self.device) for j in srcs}
-        self.v = {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, self.device) for j in srcs}
+        shared = self._shared_kv or {"k": {}, "v": {}}
+        self.k = {j: shared["k"][j] if j in shared["k"] else to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype,
+                                                                        self.device) for j in srcs}
+        self.v = {j: shared["v"][j] if j in shared["v"] else to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype,
+                                                                        self.device) for j in srcs}
         self.kv_segs = {j: rba.make_segs(w.rank_runs(j)) for j in srcs}
         return self.order
 
@@ -120,25 +129,31 @@ class RingReplay:
         return rba.rba_fwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
                                 self.kv_segs[s.src], o, l, stream)
 
-    def forward(self, stream=None, on_step=None, fused_merge: bool = True) -> torch.Tensor:
+    def forward(self, stream=None, on_step=None, fused_merge: bool = True, resume: bool = False) -> torch.Tensor:
         """Replay all steps; returns o_final (merged output in the input dtype).
 
         The first live step writes the running result (o_acc, lse_acc); each
         later one is merged into it by rba_fwd_step_acc in the same launch
         (``fused_merge``, the last one also writing o_final), or, with
         ``fused_merge=False``, goes through o_part / lse_part and rba_merge.
+        With ``resume`` (fused merges only) (o_acc, lse_acc) already hold the
+        result of earlier steps, restored by the caller, and every step is
+        merged into it.
         ``on_step(kind, i)`` is called before each launch ("fwd" / "merge") so
         a caller can bracket launches with events.
         """
         live = [i for i, s in enumerate(self.steps) if s.status == rba.RBA_OK]
         final_dtype = rba.RBA_BF16 if self.dtype == rba.RBA_BF16 else rba.RBA_F32
+        if resume and not fused_merge:
+            raise ValueError("resume merges every step in its launch (fused_merge=True)")
         if not live:
-            self.o_acc.zero_()
-            self.lse_acc.fill_(float("-inf"))
-            self.o_final.zero_()
+            if not resume:
+                self.o_acc.zero_()
+                self.lse_acc.fill_(float("-inf"))
+            rba.rba_merge(self.o_acc, self.lse_acc, None, None, self.o_final, final_dtype, stream)
             return self.o_final
         for n_done, i in enumerate(live):
-            first = n_done == 0
+            first = n_done == 0 and not resume
             last = n_done == len(live) - 1
             if on_step:
                 on_step("fwd", i)
@@ -155,7 +170,7 @@ class RingReplay:
                     on_step("merge", i)
                 rba.rba_merge(self.o_acc, self.lse_acc, self.o_part, self.lse_part,
                               self.o_final if last else None, final_dtype, stream)
-        if len(live) == 1:
+        if len(live) == 1 and not resume:
             rba.rba_merge(self.o_acc, self.lse_acc, None, None, self.o_final, final_dtype, stream)
         return self.o_final
 

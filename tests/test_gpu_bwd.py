@@ -12,7 +12,7 @@ from ring_sequence_parallelism_amd import rba
 from ring_sequence_parallelism_amd import workloads as W
 from ring_sequence_parallelism_amd.ring import RingReplay, to_device
 
-from _gpu_util import assert_close, chunk_positions, cu_or_none, full_kv_f64
+from _gpu_util import assert_close, chunk_positions, cu_or_none, full_kv_f64, oracle_backward_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,22 +28,33 @@ def _bf16(rng, shape):
 
 
 def test_preprocess():
+    """delta = rowsum(dO * O) against the oracle's delta: the oracle's own
+    fp64 output (rounded to fp32, the form of the merged accumulator the
+    backward uses) and dO go in, the oracle's delta is the expected value."""
     _say("bwd preprocess")
     rng = np.random.default_rng(1)
     for d in (64, 128):
-        ob, o64 = _bf16(rng, (333, 6, d))
-        db, d64 = _bf16(rng, (333, 6, d))
-        delta = torch.empty((6, 333), device=DEV)
+        sq, sk, hq, hkv = 333, 200, 6, 2
+        _, q64 = _bf16(rng, (sq, hq, d))
+        _, k64 = _bf16(rng, (sk, hkv, d))
+        _, v64 = _bf16(rng, (sk, hkv, d))
+        db, do64 = _bf16(rng, (sq, hq, d))
+        scale = float(np.float32(1 / np.sqrt(d)))
+        qpos, kpos = np.arange(100, 100 + sq), np.arange(sk)
+        _, _, _, want_delta, o64, _ = oracle.attention_backward(q64, k64, v64, do64, qpos, kpos,
+                                                                 oracle.MASK_CAUSAL, scale)
+        delta = torch.full((hq, sq), float("nan"), device=DEV)
+        o32 = torch.from_numpy(o64.astype(np.float32)).to(DEV)
+        rba.rba_bwd_preprocess(o32, to_device(db, "bf16", DEV), delta)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(delta.cpu().numpy(), want_delta, rtol=1e-5, atol=2e-6)
+        # bf16 O (the rounded final output) and bf16 dO: the same definition on
+        # the bf16 values given
+        ob = W.f32_to_bf16_bits(o64.astype(np.float32))
         rba.rba_bwd_preprocess(to_device(ob, "bf16", DEV), to_device(db, "bf16", DEV), delta)
         torch.cuda.synchronize()
-        want = (o64 * d64).sum(axis=2).T
-        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-4)
-        # fp32 output (the merged accumulator) with a bf16 gradient
-        of = rng.standard_normal((333, 6, d)).astype(np.float32)
-        rba.rba_bwd_preprocess(torch.from_numpy(of).to(DEV), to_device(db, "bf16", DEV), delta)
-        torch.cuda.synchronize()
-        want = (of.astype(np.float64) * d64).sum(axis=2).T
-        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-4)
+        want = (W.bf16_bits_to_f32(ob).astype(np.float64) * do64).sum(axis=2).T
+        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=2e-6)
 
 
 def _pos(segs):
@@ -158,35 +169,27 @@ def test_replay_packed_docs_scaled():
         assert_close(dv[j], wdv[kp], "bf16", f"dv src {j}")
 
 
-def test_replay_c5_full_sampled():
+def test_replay_c5_full():
+    """The 32K backward workload: rank 3's whole dQ (4096 rows, 32 heads) and
+    the per-step dK / dV of all 32768 keys and 8 KV heads, placed at their
+    chunks' positions, against the fp64 gradient of full causal attention."""
     w = W.WORKLOADS["c5"]
     _say("bwd replay full", w.name)
     rr, dq, dk, dv = _replay_grads(w, w.rank)
-    rows = W.gen_sampled_rows(w, 48, w.chunk_len)
     q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, rr.r), w.dtype)
     do64 = W.to_f64(W.gen_rank_chunk(w, W.T_DO, rr.r), w.dtype)
     k64, v64 = full_kv_f64(w)
-    rng = np.random.default_rng(55)
-    keys = np.sort(rng.choice(w.seq, 64, replace=False))
-    group = w.hq // w.hkv
-    for g in (0, w.hkv - 1):
-        heads = list(range(g * group, (g + 1) * group))
-        wdq, wdk, wdv = oracle.attention_backward_sampled(
-            q64, k64, v64, do64, chunk_positions(w, rr.r), np.arange(w.seq), w.mask, w.scale,
-            rows=rows, keys=keys, heads=heads)
-        assert_close(dq[rows][:, heads], wdq, "bf16", f"dq group {g}")
-        # gather each sampled key's per-step gradient from the chunk that holds it
-        got_k = np.zeros((len(keys), w.d))
-        got_v = np.zeros((len(keys), w.d))
-        for j in dk:
-            kp = chunk_positions(w, j)
-            where = {int(p): i for i, p in enumerate(kp)}
-            for t, key in enumerate(keys):
-                if int(key) in where:
-                    got_k[t] = dk[j][where[int(key)], g]
-                    got_v[t] = dv[j][where[int(key)], g]
-        assert_close(got_k, wdk[:, g], "bf16", f"dk group {g}")
-        assert_close(got_v, wdv[:, g], "bf16", f"dv group {g}")
+    wdq, wdk, wdv, _, _ = oracle_backward_rows(q64, k64, v64, do64, chunk_positions(w, rr.r), w.mask, w.scale)
+    assert_close(dq, wdq, "bf16", "dq")
+    got_k = np.zeros_like(wdk)
+    got_v = np.zeros_like(wdv)
+    for j in dk:
+        kp = chunk_positions(w, j)
+        got_k[kp] = dk[j]
+        got_v[kp] = dv[j]
+    assert len(dk) == w.n_ranks
+    assert_close(got_k, wdk, "bf16", "dk (all keys)")
+    assert_close(got_v, wdv, "bf16", "dv (all keys)")
 
 
 # ---------------------------------------------------------------------------

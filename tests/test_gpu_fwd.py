@@ -11,9 +11,10 @@ import torch
 import oracle
 from ring_sequence_parallelism_amd import rba
 from ring_sequence_parallelism_amd import workloads as W
-from ring_sequence_parallelism_amd.ring import RingReplay, to_device
+from ring_sequence_parallelism_amd.ring import RingReplay, ring_order, to_device
 
-from _gpu_util import assert_close, assert_lse, chunk_positions, cu_or_none, full_kv_f64
+from _gpu_util import (BF16_MAX, BF16_MEAN, assert_close, assert_lse, chunk_positions, cu_or_none, full_kv_f64,
+                       oracle_attention_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -233,7 +234,8 @@ def _check_replay(w, rank, rows=None, heads=None):
     k64, v64 = full_kv_f64(w)
     if rows is not None:
         qpos, q64 = qpos[rows], q64[rows]
-    want_o, want_l = oracle.attention(q64, k64, v64, qpos, np.arange(w.seq), w.mask, w.scale, cu_or_none(w))
+    want_o, want_l = oracle_attention_rows(q64, k64, v64, qpos, w.mask, w.scale, cu_or_none(w),
+                                           block=64 if rows is None else 8)
     got = rr.o_final.float().cpu().numpy()
     got_l = rr.lse_acc.cpu().numpy()
     if rows is not None:
@@ -271,26 +273,129 @@ def test_replay_packed_docs_scaled(rank):
     _check_replay(w, rank)
 
 
-def test_replay_c2_full_sampled_rows():
+def test_replay_c2_full():
+    """The 32K causal zigzag workload: all 4096 rows of rank 3, all 32 heads,
+    against unchunked attention over the whole sequence."""
     w = W.WORKLOADS["c2"]
-    _say("replay full", w.name)
-    rows = W.gen_sampled_rows(w, 256, w.chunk_len)
-    _check_replay(w, w.rank, rows)
+    _say("replay full", w.name, "all rows")
+    _check_replay(w, w.rank)
 
 
-@pytest.mark.parametrize("rank", [0, 6, 15])
-def test_replay_c3_full_sampled_rows(rank):
+def test_replay_c3_full_all_ranks():
+    """The 64K packed-document workload: every rank replays all 16 KV chunks
+    (256 calls, the host skips the empty ones); the 16 ranks' outputs together
+    are compared with the full 65536-row packed causal attention."""
     w = W.WORKLOADS["c3"]
-    _say("replay full", w.name, "rank", rank)
-    rows = W.gen_sampled_rows(w, 128, w.chunk_len)
-    _check_replay(w, rank, rows)
+    _say("replay full", w.name, "all 16 ranks")
+    k64, v64 = full_kv_f64(w)
+    cu = cu_or_none(w)
+    shared = {"k": {j: to_device(W.gen_rank_chunk(w, W.T_K, j), w.dtype, DEV) for j in range(w.n_ranks)},
+              "v": {j: to_device(W.gen_rank_chunk(w, W.T_V, j), w.dtype, DEV) for j in range(w.n_ranks)}}
+    abs_sum, count, o_max, l_max, launched = 0.0, 0, 0.0, 0.0, 0
+    for r in range(w.n_ranks):
+        rr = RingReplay(w, r, DEV, kv=shared)
+        launched += sum(s.status == rba.RBA_OK for s in rr.steps)
+        rr.forward()
+        torch.cuda.synchronize()
+        got = rr.o_final.float().cpu().numpy().astype(np.float64)
+        got_l = rr.lse_acc.cpu().numpy()
+        qpos = chunk_positions(w, r)
+        q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, r), w.dtype)
+        want_o, want_l = oracle_attention_rows(q64, k64, v64, qpos, w.mask, w.scale, cu)
+        assert_lse(got_l, want_l, f"rank {r} lse")
+        err = np.abs(got - want_o)
+        assert np.isfinite(got).all(), f"rank {r}: non-finite output"
+        abs_sum += float(err.sum())
+        count += err.size
+        o_max = max(o_max, float(err.max()))
+        l_max = max(l_max, float(np.abs(got_l - want_l).max()))
+        del rr
+    mean = abs_sum / count
+    print(f"[c3] {launched} non-empty calls of 256; o max {o_max:.3g} mean {mean:.3g}; lse max {l_max:.3g}",
+          flush=True)
+    assert o_max <= BF16_MAX and mean <= BF16_MEAN, (o_max, mean)
 
 
 def test_replay_c4_full_sampled_rows():
+    """The 512K causal zigzag workload: the 256 sampled query rows the
+    workload names (first and last row of each piece, the rest drawn
+    uniformly), all 32 heads, in fp64."""
     w = W.WORKLOADS["c4"]
-    _say("replay full", w.name)
-    rows = W.gen_sampled_rows(w, 48, w.chunk_len)
+    _say("replay full", w.name, "256 sampled rows")
+    rows = W.gen_sampled_rows(w, 256, w.chunk_len)
+    assert rows.size == 256
     _check_replay(w, w.rank, rows)
+
+
+# ---------------------------------------------------------------------------
+# replays that must fail, and replays that must pass, the comparison
+
+def _teeth_workload():
+    return W.scaled_workload(W.WORKLOADS["c2"], 4096, hq=8, hkv=2, name="c2_s4096_teeth")
+
+
+def _replay_error(w, rank, order):
+    rr = RingReplay(w, rank, DEV, order=order)
+    rr.forward()
+    torch.cuda.synchronize()
+    q64 = W.to_f64(W.gen_rank_chunk(w, W.T_Q, rank), w.dtype)
+    k64, v64 = full_kv_f64(w)
+    want_o, want_l = oracle_attention_rows(q64, k64, v64, chunk_positions(w, rank), w.mask, w.scale)
+    return rr, rr.o_final.float().cpu().numpy(), rr.lse_acc.cpu().numpy(), want_o, want_l
+
+
+@pytest.mark.parametrize("change", ["drop", "duplicate"])
+def test_replay_with_a_missing_or_repeated_step_fails(change):
+    """A ring that skips one KV chunk, or visits one twice, is not exact
+    attention: the comparison that the true ring passes must reject it."""
+    w = _teeth_workload()
+    rank = 5
+    order = ring_order(rank, w.n_ranks)
+    order = order[:3] + order[4:] if change == "drop" else order + [order[2]]
+    _say("replay teeth", change, order)
+    _, got, got_l, want_o, want_l = _replay_error(w, rank, order)
+    with pytest.raises(AssertionError):
+        assert_lse(got_l, want_l, "lse")
+        assert_close(got, want_o, "bf16", "o")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_replay_permuted_order_passes(seed):
+    """The merge is order-free: the KV chunks in any order give the same
+    attention (to rounding)."""
+    w = _teeth_workload()
+    rank = 2
+    order = list(np.random.default_rng(seed).permutation(ring_order(rank, w.n_ranks)))
+    _say("replay permuted", order)
+    _, got, got_l, want_o, want_l = _replay_error(w, rank, order)
+    assert_lse(got_l, want_l, "lse")
+    assert_close(got, want_o, "bf16", "o")
+
+
+@pytest.mark.parametrize("k", [1, 4, 7])
+def test_replay_checkpoint_resume(k):
+    """Stop after k steps, copy the running (O, LSE) to host memory, restore it
+    into fresh buffers and finish the remaining steps: the result is bit for
+    bit that of the uninterrupted replay."""
+    w = _teeth_workload()
+    rank = 6
+    order = ring_order(rank, w.n_ranks)
+    _say("replay checkpoint after", k, "steps")
+    full = RingReplay(w, rank, DEV)
+    full.forward()
+    head = RingReplay(w, rank, DEV, order=order[:k])
+    head.forward()
+    torch.cuda.synchronize()
+    saved_o, saved_l = head.o_acc.cpu().clone(), head.lse_acc.cpu().clone()
+    del head
+    tail = RingReplay(w, rank, DEV, order=order[k:])
+    tail.o_acc.copy_(saved_o.to(DEV))
+    tail.lse_acc.copy_(saved_l.to(DEV))
+    tail.forward(resume=True)
+    torch.cuda.synchronize()
+    assert torch.equal(tail.o_acc, full.o_acc)
+    assert torch.equal(tail.lse_acc, full.lse_acc)
+    assert torch.equal(tail.o_final, full.o_final)
 
 
 def test_per_step_partials_c2():
