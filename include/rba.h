@@ -149,6 +149,48 @@ int rba_fwd_step_acc(const rba_attn* a,
                      float* o_acc, float* lse_acc, void* o_final, int32_t final_dtype, void* stream);
 
 /*
+ * rba_fwd_step_ws — rba_fwd_step (accumulate = 0: o, lse are the partial
+ * o_part, lse_part) or rba_fwd_step_acc (accumulate = 1: o, lse are the
+ * running o_acc, lse_acc, and o_final may be given) with a caller-provided
+ * workspace, which lets a step whose rows with work are too few to fill the
+ * GPU spread each row group's keys over several workgroups.  Defining
+ * passages: the forward step above, and HSAP's sequence-aware scheduling of
+ * irregular attention patterns (HSAP page, "Technical Contribution" and
+ * "Methodology": device-specific work schedules for packed sequences, read
+ * here at the level of one GPU's workgroups).
+ *   Same arithmetic as the unsplit step: every row's keys are covered once;
+ *   a split row group's items each produce a partial (O, LSE) over a run of
+ *   its key tiles, and a second launch on `stream` merges them with the
+ *   LSE-weighted merge of rba_merge before the result is written or merged
+ *   into the running output.  Results equal the unsplit step's up to the
+ *   rounding of the extra merges.
+ *   workspace: device memory, 16-byte aligned, owned by the caller, at least
+ *   workspace_bytes bytes; NULL (or too small for any split) = never split.
+ *   Its contents on entry do not matter and are overwritten; it must not be
+ *   shared with another call in flight.  rba_fwd_workspace_size gives the
+ *   bytes a step would use (at most 32 MiB).
+ * Same inputs, limits, errors and RBA_STEP_EMPTY behaviour as rba_fwd_step /
+ * rba_fwd_step_acc; accumulate = 0 with a non-NULL o_final is
+ * RBA_ERR_INVALID.  fp32 steps never split.
+ */
+int rba_fwd_step_ws(const rba_attn* a,
+                    const void* q, int64_t sq, const rba_segs* q_segs,
+                    const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                    float* o, float* lse, int32_t accumulate, void* o_final, int32_t final_dtype,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * rba_fwd_workspace_size — host-side query (reads the current device's
+ * compute-unit count, launches nothing): *bytes = the workspace
+ * rba_fwd_step_ws would use for this step (0 when it would not split), at
+ * most 32 MiB.  Returns RBA_OK, RBA_STEP_EMPTY (*bytes = 0) or an argument
+ * error as rba_fwd_step.  Document-masked steps split only with
+ * cu_seqlens_host.
+ */
+int rba_fwd_workspace_size(const rba_attn* a, int64_t sq, const rba_segs* q_segs,
+                           int64_t sk, const rba_segs* kv_segs, int64_t* bytes);
+
+/*
  * rba_merge — LSE-weighted merge of a step's partial into the running result.
  * Defining passage: the blockwise exact attention the TASP page builds on
  * (FlashAttention and "Self-attention Does Not Need O(n^2) Memory", both in

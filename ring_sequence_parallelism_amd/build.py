@@ -22,6 +22,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librba.so")
 
 SOURCES = ["rba_host.cpp", "rba_fwd.hip", "rba_merge.hip", "rba_bwd.hip"]
+# measurement probes for the benchmark (MFMA loop, HBM copy): a library of
+# their own, not part of the step ABI
+PROBE_SOURCES = ["rba_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "librba_probe.so")
 ARCH = "gfx950"
 
 
@@ -58,19 +62,25 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link librba.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link librba.so and librba_probe.so; returns
+    the path of librba.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -58,9 +58,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const WaveTask t = make_task<QR>(p, wave, blockIdx.x);
   TileIter it{-1, 0, 0, 0, 1};
   tile_next(it, p, t);
+  // a split item starts t.skip tiles into its row group's visit list and
+  // computes at most t.count tiles
+  for (int i = 0; i < t.skip && it.valid; ++i) tile_next(it, p, t);
+  int left = t.count;
   // A merging step whose rows see no key tile leaves the running result as
   // it is (an empty partial merges as the identity).
-  if (!it.valid && p.accumulate && !p.o_final) return;
+  if (!it.valid && t.slot < 0 && p.accumulate && !p.o_final) return;
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   bf16x8 qreg[NQB][D / 16];
@@ -77,16 +81,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       qreg[qb][ks] = ok ? src[2 * ks + half] : z;
     }
     qpos[qb] = (ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
-    qds[qb] = (ok && !FULL && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos[qb]) : INT32_MIN;
+    qds[qb] = (ok && !FULL && p.mask == kMaskDoc) ? wave_doc_start(p, t, qpos[qb]) : INT32_MIN;
   }
 
   const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
 
   f32x16 oacc[NQB][D / 32];
-  float m_run[NQB], l_run[NQB];
+  // Running maximum in base-2 units (m_run), the same with -inf read as 0
+  // (m_use, the reference the exponentials subtract) and the raw score
+  // above which the lazy maximum must move ((m_run + 8) / scale_log2).
+  float m_run[NQB], m_use[NQB], thr_raw[NQB], l_run[NQB];
+  const float inv_c = 1.f / p.scale_log2;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m_run[qb] = -INFINITY;
+    m_use[qb] = 0.f;
+    thr_raw[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
@@ -106,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     TileIter nx = it;
     tile_next(nx, p, t);
+    if (--left == 0) nx.valid = 0;
     if (nx.valid) loader.issue(nx.kt, buf ^ 1);
 
     // A tile this wave may skip (another wave of the workgroup needs it) is
@@ -163,31 +174,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       // 256 and most tiles skip the rescale.
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        // The tile maximum is compared in raw score units; it is scaled only
+        // when the running maximum moves.
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][qb][j]);
-        mx = half_max(mx) * p.scale_log2;
-        if (__any(mx > m_run[qb] + 8.f)) {
-          const float m_new = fmaxf(m_run[qb], mx);
+        mx = half_max(mx);
+        if (__any(mx > thr_raw[qb])) {
+          const float m_new = fmaxf(m_run[qb], mx * p.scale_log2);
           const float alpha = fast_exp2(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
           m_run[qb] = m_new;
+          m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+          thr_raw[qb] = (m_new + 8.f) * inv_c;
           l_run[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
         }
-        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-        float lsum = 0.f;
+        // four partial sums: shorter dependency chains for the scheduler
+        float ls[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float e = fast_exp2(fmaf(sacc[kb][qb][j], p.scale_log2, -m_use));
+            const float e = fast_exp2(fmaf(sacc[kb][qb][j], p.scale_log2, -m_use[qb]));
             sacc[kb][qb][j] = e;
-            lsum += e;
+            const int i = (16 * kb + j) & 3;
+            ls[i] = (kb == 0 && j < 4) ? e : ls[i] + e;
           }
-        l_run[qb] += lsum;
+        l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
 
       // O^T += V^T P^T.  The k-slot of P^T register j maps to key
@@ -232,7 +248,102 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     const bool has = l > 0.f;
     const float inv = has ? 1.f / l : 0.f;
     const float lse = has ? m_run[qb] * kLn2 + __logf(l) : -INFINITY;
-    write_step_output<D>(p, t.row0 + qb * 32 + col, t.h, half, oacc[qb], inv, lse);
+    if (t.slot >= 0)
+      write_split_partial<D>(p, t.slot, wave, col, half, oacc[qb], inv, lse);
+    else
+      write_step_output<D>(p, t.row0 + qb * 32 + col, t.h, half, oacc[qb], inv, lse);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split items: one workgroup per (split row group, head group) with
+// the forward workgroup's 4 (head, row block) waves; 8 lanes per row (D / 32
+// f32x4 vectors each), so a wave covers 8 rows and runs 4 passes over its 32.
+// The items' partials (O_s normalized, LSE_s) combine as
+//   L = m + ln sum_s e^{LSE_s - m},  O = sum_s e^{LSE_s - L} O_s   (m = max LSE_s),
+// the LSE-weighted merge of all items at once; items with LSE = -inf weigh 0.
+// The LSE values are read first and then every O_s load is issued before
+// any is used (the kernel is bound by load latency).  The result goes to the
+// output as write_step_output would write an unsplit partial.
+
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(FwdParams p) {
+  constexpr int VPL = D / 32;                      // f32x4 vectors per lane
+  constexpr int MAXI = 8;                          // items read per batch
+  const int hg = blockIdx.x % p.n_head_groups;
+  const int i = blockIdx.x / p.n_head_groups;      // order index, < n_split_rg
+  const int rg = p.order[i];
+  const int it0 = p.item_start[i], n_it = p.item_start[i + 1] - it0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = hg * p.hpw + wave % p.hpw;
+  const int v0 = (lane & 7) * VPL;
+  const size_t slot_stride = (size_t)p.n_head_groups * split_slot_floats(D);
+  const float* slot0 = p.ws + (size_t)(it0 * p.n_head_groups + hg) * split_slot_floats(D);
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rin = pass * 8 + (lane >> 3);
+    const int row = rg * p.rbw * 32 + (wave / p.hpw) * 32 + rin;
+    // largest item LSE of the row
+    float m = -INFINITY;
+    for (int s = 0; s < n_it; ++s) m = fmaxf(m, slot0[s * slot_stride + 128 * D + wave * 32 + rin]);
+    f32x4 o[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      for (int s0 = 0; s0 < n_it; s0 += MAXI) {
+        const int ns = min(MAXI, n_it - s0);
+        float w[MAXI];
+        f32x4 os[MAXI][VPL];
+#pragma unroll
+        for (int s = 0; s < MAXI; ++s)
+          if (s < ns) {
+            const float* slot = slot0 + (s0 + s) * slot_stride;
+            w[s] = __expf(slot[128 * D + wave * 32 + rin] - m);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+              os[s][v] = reinterpret_cast<const f32x4*>(slot + (size_t)(wave * 32 + rin) * D)[v0 + v];
+          }
+#pragma unroll
+        for (int s = 0; s < MAXI; ++s)
+          if (s < ns) {
+            wsum += w[s];
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) o[v] += w[s] * os[s][v];
+          }
+      }
+      const float inv = 1.f / wsum;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) o[v] *= inv;
+    }
+    const float L = m == -INFINITY ? -INFINITY : m + __logf(wsum);
+    if (row >= p.sq) continue;
+    const size_t li = (size_t)h * p.sq + row;
+    const size_t oi = ((size_t)row * p.hq + h) * D + 4 * v0;
+    float* dst = p.o + oi;
+    if (!p.accumulate) {
+      if ((lane & 7) == 0) p.lse[li] = L;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) reinterpret_cast<f32x4*>(dst)[v] = o[v];
+      continue;
+    }
+    // The 8 lanes of the row (one wave) read the running LSE before one of
+    // them writes it.
+    if (L == -INFINITY && !p.o_final) continue;
+    const MergeWeights mw = merge_weights(p.lse[li], L);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const f32x4 r = mw.wa * reinterpret_cast<const f32x4*>(dst)[v] + mw.wb * o[v];
+      reinterpret_cast<f32x4*>(dst)[v] = r;
+      if (p.o_final) {
+        if (p.final_bf16) {
+          const u32x2 b = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+          reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi)[v] = b;
+        } else {
+          reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi)[v] = r;
+        }
+      }
+    }
+    if ((lane & 7) == 0) p.lse[li] = mw.L;
   }
 }
 
@@ -263,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
     for (int ks = 0; ks < D / 2; ++ks) qreg[ks] = row_ok ? src[2 * ks + half] : 0.f;
   }
   const int32_t qpos = row_ok ? row_to_pos(p.qs, row) : kPosNone;
-  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? doc_start(p.cu, p.n_docs, qpos) : INT32_MIN;
+  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? wave_doc_start(p, t, qpos) : INT32_MIN;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -370,6 +481,17 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, true>), grid, block, 0, s, p);
   else if (d == 64)
     hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, false>), grid, block, 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const FwdParams& p, int d, hipStream_t s) {
+  dim3 grid(p.n_split_rg * p.n_head_groups), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((split_merge_kernel<128>), grid, block, 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL((split_merge_kernel<64>), grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

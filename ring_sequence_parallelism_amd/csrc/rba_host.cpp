@@ -320,11 +320,13 @@ int64_t host_doc_start(const DocTable& dt, int64_t p) {
 // interval (the interval its workgroup walks: up to the group's last
 // position, from the document start of its first position under the
 // document mask), and groups are sorted by decreasing work (stable).  Left
-// in natural order without a mask (all equal), without the host copy of
-// cu_seqlens, or beyond kMaxOrder groups.
+// in natural order without a mask (all equal) or without the host copy of
+// cu_seqlens.  Beyond kMaxOrder groups only the reversed natural order is
+// available (when it is heavy-first).
 void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::FwdParams& p, int64_t rows_per_wg) {
   p.n_order = 0;
-  if (a->mask == RBA_MASK_NONE || p.n_row_groups > rba::kMaxOrder) return;
+  p.order_reverse = 0;
+  if (a->mask == RBA_MASK_NONE) return;
   if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu) return;
   std::vector<std::pair<int64_t, int>> work(p.n_row_groups);
   for (int rg = 0; rg < p.n_row_groups; ++rg) {
@@ -335,6 +337,21 @@ void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fw
     int64_t w = 0;
     for (const Seg& s : plan.ks) w += keys_in(s, std::max(k_lo, INT64_MIN / 4), k_hi);
     work[rg] = {w, rg};
+  }
+  if (p.n_row_groups > rba::kMaxOrder) {
+    // Too many groups to list in the kernel arguments.  When the work never
+    // decreases along the rows (a causal chunk whose positions ascend, such
+    // as a zigzag rank's own step) and is not all equal, the reversed
+    // natural order is heavy-first: each XCD then starts groups of similar
+    // length together, whose workgroups walk the same key tiles at the same
+    // time and share them in L2.
+    bool rising = true, equal = true;
+    for (int rg = 1; rg < p.n_row_groups; ++rg) {
+      rising = rising && work[rg].first >= work[rg - 1].first;
+      equal = equal && work[rg].first == work[0].first;
+    }
+    p.order_reverse = (rising && !equal) ? 1 : 0;
+    return;
   }
   std::stable_sort(work.begin(), work.end(), [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
     return x.first > y.first;
@@ -403,11 +420,108 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   return RBA_OK;
 }
 
-// Shared body of rba_fwd_step (partial written to o / lse) and
-// rba_fwd_step_acc (partial merged into the running o / lse).
+// Rows [a, b) of segment k whose positions lie in [lo, hi] (a >= b: none),
+// as the device's rows_in computes them.
+std::pair<int64_t, int64_t> host_rows_in(const Seg& k, int64_t lo, int64_t hi) {
+  const int64_t a = std::min(k.len, std::max<int64_t>(0, -floor_div(k.start - lo, k.stride)));
+  const int64_t b = std::min(k.len, std::max<int64_t>(0, floor_div(hi - k.start, k.stride) + 1));
+  return {a, b};
+}
+
+// Number of key tiles the query-stationary workgroup of rows [r0, r1)
+// visits: the host form of the device's tile iterator (per KV segment in row
+// order, the tiles holding rows whose positions lie in the workgroup's
+// allowed interval, each tile once).
+int64_t visited_tiles(const rba_attn* a, const StepPlan& plan, int64_t r0, int64_t r1) {
+  constexpr int64_t BN = rba::kFwdTileKeys;
+  const auto pr = host_pos_range(plan.qs, r0, r1);
+  int64_t k_lo = INT64_MIN / 4, k_hi = INT64_MAX / 4;
+  if (a->mask != RBA_MASK_NONE) k_hi = pr.second;
+  if (a->mask == RBA_MASK_DOC_CAUSAL) k_lo = host_doc_start(plan.dt, pr.first);
+  int64_t next_tile = 0, count = 0;
+  for (const Seg& k : plan.ks) {
+    const auto rs = host_rows_in(k, k_lo, k_hi);
+    if (rs.first >= rs.second) continue;
+    const int64_t t0 = std::max((k.row0 + rs.first) / BN, next_tile);
+    const int64_t t1 = (k.row0 + rs.second + BN - 1) / BN;
+    if (t1 > t0) count += t1 - t0;
+    next_tile = std::max(next_tile, t1);
+  }
+  return count;
+}
+
+// Largest workspace a forward launch splits into (bytes).
+constexpr int64_t kSplitMaxBytes = int64_t(32) << 20;
+// A launch splits only when its heaviest row group visits at least this many
+// key tiles: each workgroup's tiles follow one another at about the latency
+// of one tile load, and a split adds the partials' round trip and a merge
+// launch (roughly the time of 8-10 such tiles), so shorter lists gain nothing.
+constexpr int64_t kSplitMinTiles = 32;
+
+// Split plan of a forward launch (see FwdParams): when the row groups with
+// work give fewer workgroups than one round of the chip (two per compute
+// unit) and the heaviest visits at least kSplitMinTiles tiles, each heavy
+// row group's visit list is cut into items so that the launch has about one
+// round, each item at least 2 tiles; the items' partials then need
+// split_slot_floats(d) floats of workspace per item and head group, at most
+// `ws_limit` bytes (fewer, longer items otherwise).
+// Returns the workspace bytes the plan uses (0: no split, p unchanged).
+int64_t plan_split(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::FwdParams& p, int64_t ws_limit) {
+  p.split = 0;
+  if (a->dtype != RBA_BF16 || p.n_row_groups > rba::kMaxOrder) return 0;
+  if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu) return 0;
+  const int64_t rows_per_wg = (int64_t)p.rbw * 32;
+  std::vector<std::pair<int64_t, int>> tiles(p.n_row_groups);
+  int64_t total = 0, n_active = 0;
+  for (int rg = 0; rg < p.n_row_groups; ++rg) {
+    const int64_t r0 = rg * rows_per_wg;
+    tiles[rg] = {visited_tiles(a, plan, r0, std::min(sq, r0 + rows_per_wg)), rg};
+    total += tiles[rg].first;
+    n_active += tiles[rg].first > 0;
+  }
+  const int64_t slots = 2 * (int64_t)device_cus();
+  if (n_active == 0 || n_active * p.n_head_groups >= slots) return 0;
+  int64_t max_tiles = 0;
+  for (const auto& t : tiles) max_tiles = std::max(max_tiles, t.first);
+  if (max_tiles < kSplitMinTiles) return 0;
+  std::stable_sort(tiles.begin(), tiles.end(), [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
+    return x.first > y.first;
+  });
+  const int64_t slot_bytes = rba::split_slot_floats(a->d) * 4;
+  int64_t L = std::max<int64_t>(2, (total * p.n_head_groups + slots - 1) / slots);
+  for (;; L *= 2) {
+    int n_split = 0;
+    int64_t items = 0;
+    while (n_split < n_active && (tiles[n_split].first + L - 1) / L > 1) {
+      items += (tiles[n_split].first + L - 1) / L;
+      ++n_split;
+    }
+    if (n_split == 0) return 0;
+    const int64_t bytes = items * p.n_head_groups * slot_bytes;
+    if (n_split > rba::kMaxSplitRg || items > 60000 || bytes > std::min(ws_limit, kSplitMaxBytes)) continue;
+    // the plan
+    for (int i = 0; i < p.n_row_groups; ++i) p.order[i] = (uint16_t)tiles[i].second;
+    p.item_start[0] = 0;
+    for (int i = 0; i < n_split; ++i) {
+      const int64_t t = tiles[i].first, n = (t + L - 1) / L;
+      p.split_len[i] = (uint16_t)((t + n - 1) / n);   // n items of nearly equal length
+      p.item_start[i + 1] = (uint16_t)(p.item_start[i] + n);
+    }
+    p.split = 1;
+    p.n_active = (int32_t)n_active;
+    p.n_split_rg = n_split;
+    p.n_items = (int32_t)(items + (n_active - n_split));
+    p.n_wg = (int32_t)((int64_t)p.n_head_groups * (p.n_items + p.n_row_groups - n_active));
+    return bytes;
+  }
+}
+
+// Shared body of the forward entry points: the partial written to o / lse,
+// or merged into the running o / lse (accumulate); with a workspace of
+// ws_bytes bytes a launch with too few workgroups may be split (plan_split).
 int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
              int64_t sk, const rba_segs* kv_segs, float* o, float* lse, bool accumulate, void* o_final,
-             int32_t final_dtype, void* stream) {
+             int32_t final_dtype, void* stream, void* ws = nullptr, int64_t ws_bytes = 0) {
   g_err.clear();
   StepPlan plan;
   int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
@@ -433,8 +547,29 @@ int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
   p.o_final = o_final;
   p.final_bf16 = final_dtype == RBA_BF16;
   if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, bf16), p))) return rc;
+  if (ws) {
+    if ((rc = check_ptr(ws, "workspace"))) return rc;
+    if (ws_bytes < 0) return fail(RBA_ERR_INVALID, "negative workspace size");
+    if (plan_split(a, plan, sq, p, ws_bytes) > 0) p.ws = static_cast<float*>(ws);
+  }
   hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
+  if (e == hipSuccess && p.split) e = rba::launch_split_merge(p, a->d, (hipStream_t)stream);
   return hip_status(e, "forward step");
+}
+
+// Workspace bytes a forward step would split into (0: it would not split).
+int fwd_workspace_size(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t sk, const rba_segs* kv_segs,
+                       int64_t* bytes) {
+  if (!bytes) return fail(RBA_ERR_INVALID, "bytes is NULL");
+  *bytes = 0;
+  StepPlan plan;
+  int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
+  if (rc) return rc;
+  if (plan.empty) return RBA_STEP_EMPTY;
+  rba::FwdParams p{};
+  if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, a->dtype == RBA_BF16), p))) return rc;
+  *bytes = plan_split(a, plan, sq, p, kSplitMaxBytes);
+  return RBA_OK;
 }
 
 }  // namespace
@@ -467,6 +602,23 @@ int rba_fwd_step_acc(const rba_attn* a, const void* q, int64_t sq, const rba_seg
                      const void* v, int64_t sk, const rba_segs* kv_segs, float* o_acc, float* lse_acc,
                      void* o_final, int32_t final_dtype, void* stream) {
   return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o_acc, lse_acc, true, o_final, final_dtype, stream);
+}
+
+int rba_fwd_workspace_size(const rba_attn* a, int64_t sq, const rba_segs* q_segs, int64_t sk,
+                           const rba_segs* kv_segs, int64_t* bytes) {
+  g_err.clear();
+  return fwd_workspace_size(a, sq, q_segs, sk, kv_segs, bytes);
+}
+
+int rba_fwd_step_ws(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k,
+                    const void* v, int64_t sk, const rba_segs* kv_segs, float* o, float* lse, int32_t accumulate,
+                    void* o_final, int32_t final_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!accumulate && o_final) {
+    g_err.clear();
+    return fail(RBA_ERR_INVALID, "o_final is written only when accumulating");
+  }
+  return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o, lse, accumulate != 0, o_final, final_dtype, stream,
+                  workspace, workspace_bytes);
 }
 
 int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, const float* o_part,

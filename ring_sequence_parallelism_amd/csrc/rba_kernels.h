@@ -10,6 +10,7 @@ namespace rba {
 
 constexpr int kMaxSegs = 16;
 constexpr int kMaxOrder = 512;   // longest host-computed workgroup order passed in kernel arguments
+constexpr int kMaxSplitRg = 128; // most row groups whose key range a forward launch splits
 constexpr int kFwdTileKeys = 64;   // keys per tile of the query-stationary kernels
 constexpr int kMergeThreads = 256;  // threads per workgroup of the merge and preprocess kernels
 
@@ -50,11 +51,36 @@ struct FwdParams {
   // i-th row group a head group's workgroups take is order[i].
   int32_t n_order;
   uint16_t order[kMaxOrder];
+  // 1 (only when n_order = 0): row groups are taken last to first, the
+  // heavy-first order when work rises with the row index.
+  int32_t order_reverse;
   // 1: the host has shown that every key tile a workgroup visits is full
   // (no masked pair, inside the chunk, in one segment) for every wave of it,
   // so the kernel needs no tile classification and no per-element mask.
   int32_t all_full;
+  // Split key ranges (forward only; split = 0 elsewhere).  For a launch with
+  // too few workgroups for the chip, `order` lists the row groups by
+  // decreasing number of key tiles; the first n_active have work, and the
+  // first n_split_rg of those are cut into items of split_len[i] tiles
+  // (consecutive runs of their visit list).  Item j of order index i < n_split_rg is work item
+  // item_start[i] + j; it runs in its own workgroup (per head group) and
+  // writes its partial result to workspace slot (item * n_head_groups +
+  // head group) of split_slot_floats floats; split_merge_kernel merges the
+  // slots of each split row group into the output.  The other active row
+  // groups are one item each, numbered after the split ones, and write the
+  // output directly; row groups without work follow (one workgroup each).
+  int32_t split;
+  int32_t n_active;
+  int32_t n_split_rg;
+  int32_t n_items;        // items of the n_active row groups
+  uint16_t item_start[kMaxSplitRg + 1];
+  uint16_t split_len[kMaxSplitRg];   // tiles per item of each split row group (the last may have fewer)
+  float* ws;              // workspace of the split items
 };
+
+// Floats of one split item's workspace slot: the partial (O normalized, LSE)
+// of the 4 waves x 32 rows of a query-stationary workgroup.
+constexpr int64_t split_slot_floats(int d) { return 4 * 32 * (int64_t)d + 4 * 32; }
 
 // Backward step, dK / dV kernel (key-stationary).
 struct BwdParams {
@@ -129,6 +155,9 @@ struct PrepParams {
 
 // Launchers (defined next to their kernels).  Each returns the launch status.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
+// Merges the split items' partials into the output (after launch_fwd_bf16
+// of a split launch, on the same stream).
+hipError_t launch_split_merge(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PrepParams& p, hipStream_t s);

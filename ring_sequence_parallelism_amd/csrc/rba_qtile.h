@@ -16,20 +16,57 @@ constexpr int kBN = kFwdTileKeys;  // keys per tile
 // allowed key interval of the workgroup.
 struct WaveTask {
   int g, h, row0;           // kv head, query head, first row of the wave
+  int hg;                   // head group of the workgroup
   int wg_row0, wg_rows;     // workgroup row range
   bool wave_any;            // the wave has at least one valid row
   int32_t wq_lo, wq_hi;     // wave query position range
   int32_t wds_lo, wds_hi;   // document starts of wq_lo / wq_hi (doc mask)
   int64_t k_lo, k_hi;       // allowed key positions for the workgroup
+  // split launches: the workgroup computes visited tiles [skip, skip +
+  // count) of its row group and writes its partial to workspace slot `slot`
+  // (-1: the whole visit list, written to the output)
+  int skip, count, slot;
 };
 
 template <int QR>
 __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int block) {
   const int logical = xcd_remap(block, p.n_wg);
-  const int hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
-  const int rg_i = logical % p.n_row_groups;
-  const int rg = p.n_order ? (int)p.order[rg_i] : rg_i;   // heavy first when ordered
   WaveTask t;
+  t.skip = 0;
+  t.count = INT32_MAX;
+  t.slot = -1;
+  int hg, rg;
+  if (!p.split) {
+    hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
+    const int rg_i = logical % p.n_row_groups;
+    rg = p.n_order ? (int)p.order[rg_i]
+                   : (p.order_reverse ? p.n_row_groups - 1 - rg_i : rg_i);   // heavy first when ordered
+  } else {
+    // per head group: the split items, the other active row groups, then
+    // the row groups without work
+    const int per_hg = p.n_items + p.n_row_groups - p.n_active;
+    hg = logical / per_hg;
+    const int it = logical % per_hg;
+    const int n_split_items = p.item_start[p.n_split_rg];
+    int i;
+    if (it < n_split_items) {
+      int lo = 0, hi = p.n_split_rg - 1;   // the last i with item_start[i] <= it
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)p.item_start[mid] <= it) lo = mid; else hi = mid - 1;
+      }
+      i = lo;
+      t.skip = (it - (int)p.item_start[i]) * (int)p.split_len[i];
+      t.count = p.split_len[i];
+      t.slot = it * p.n_head_groups + hg;
+    } else if (it < p.n_items) {
+      i = p.n_split_rg + (it - n_split_items);
+    } else {
+      i = p.n_active + (it - p.n_items);
+    }
+    rg = p.order[i];
+  }
+  t.hg = hg;
   const int hw = wave % p.hpw, rb = wave / p.hpw;
   t.h = hg * p.hpw + hw;
   t.g = t.h / p.group;
@@ -52,6 +89,14 @@ __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int 
   if (p.mask != kMaskNone) t.k_hi = wr.hi;
   if (p.mask == kMaskDoc) t.k_lo = doc_start(p.cu, p.n_docs, wr.lo);
   return t;
+}
+
+// Document start of a query row at position qpos of the wave: the wave's
+// own document start when all its rows lie in one document (positions
+// between wq_lo and wq_hi, whose documents start at wds_lo = wds_hi), else a
+// search of cu_seqlens for this row.
+__device__ __forceinline__ int32_t wave_doc_start(const FwdParams& p, const WaveTask& t, int32_t qpos) {
+  return t.wds_lo == t.wds_hi ? t.wds_lo : doc_start(p.cu, p.n_docs, qpos);
 }
 
 // Visits, in row order, every key tile that may hold an allowed key for the
@@ -266,6 +311,26 @@ __device__ __forceinline__ void write_step_output(const FwdParams& p, int row, i
       }
     }
   if (half == 0) p.lse[li] = w.L;
+}
+
+// Writes one lane's share of a split item's partial (O = oacc / l, the
+// row's LSE) into its workspace slot: wave w's rows at floats
+// [w * 32 * D, (w + 1) * 32 * D) (row-major, D per row), their LSE at
+// 128 * D + w * 32 + row.  Rows past the chunk hold (0, -inf).
+template <int D>
+__device__ __forceinline__ void write_split_partial(const FwdParams& p, int slot, int wave, int col, int half,
+                                                    const f32x16 (&oacc)[D / 32], float inv, float lse) {
+  float* base = p.ws + (size_t)slot * split_slot_floats(D);
+  float* dst = base + (size_t)(wave * 32 + col) * D;
+  if (half == 0) base[128 * D + wave * 32 + col] = lse;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 val = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                         oacc[db][4 * jj + 3] * inv};
+      *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * jj + 4 * half) = val;
+    }
 }
 
 }  // namespace rba

@@ -27,7 +27,8 @@ RBA_MAX_SEGS = 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
 EXPORTS = ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-           "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_last_error", "rba_version")
+           "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_fwd_step_ws", "rba_fwd_workspace_size",
+           "rba_last_error", "rba_version")
 
 
 class RbaError(RuntimeError):
@@ -99,8 +100,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rba_plan_step.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
     lib.rba_step_full_tiles.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.rba_merge_layout.argtypes = [I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    lib.rba_fwd_step_ws.argtypes = [A, P, I64, S, P, P, I64, S, P, P, I32, P, I32, P, I64, P]
+    lib.rba_fwd_workspace_size.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
     for fn in ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-               "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout"):
+               "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_fwd_step_ws", "rba_fwd_workspace_size"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
     lib.rba_last_error.argtypes = []
@@ -157,6 +160,24 @@ def rba_fwd_step_acc(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, 
     return _check("rba_fwd_step_acc", load().rba_fwd_step_acc(
         ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
         ctypes.byref(kv_segs), _ptr(o_acc), _ptr(lse_acc), _ptr(o_final), final_dtype, _stream(stream)))
+
+
+def rba_fwd_step_ws(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, o, lse, accumulate: bool,
+                    o_final=None, final_dtype: int = RBA_BF16, workspace=None, stream=None) -> int:
+    """workspace: a device tensor (its byte size is passed) or None."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _check("rba_fwd_step_ws", load().rba_fwd_step_ws(
+        ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
+        ctypes.byref(kv_segs), _ptr(o), _ptr(lse), 1 if accumulate else 0, _ptr(o_final), final_dtype,
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rba_fwd_workspace_size(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs: rba_segs) -> int:
+    """Workspace bytes rba_fwd_step_ws would use for the step (0: no split)."""
+    n = ctypes.c_int64(0)
+    _check("rba_fwd_workspace_size", load().rba_fwd_workspace_size(
+        ctypes.byref(a), sq, ctypes.byref(q_segs), sk, ctypes.byref(kv_segs), ctypes.byref(n)))
+    return n.value
 
 
 def rba_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None, final_dtype: int = RBA_BF16,

@@ -49,11 +49,16 @@ class RingReplay:
 
     def __init__(self, w: W.Workload, rank: Optional[int] = None, device="cuda",
                  kv_sources: Optional[List[int]] = None, with_grad: bool = False,
-                 order: Optional[List[int]] = None, kv: Optional[Dict[str, Dict[int, torch.Tensor]]] = None):
+                 order: Optional[List[int]] = None, kv: Optional[Dict[str, Dict[int, torch.Tensor]]] = None,
+                 workspace: Optional[torch.Tensor] = None):
         """``order``: the KV chunks of the steps in replay order (default: ring
         order; a caller may permute, drop or repeat chunks).  ``kv``: device
         K / V chunks already made for this workload ({"k": {j: tensor},
-        "v": {j: tensor}}), shared instead of generated again."""
+        "v": {j: tensor}}), shared instead of generated again.
+        ``workspace``: a device buffer handed to rba_fwd_step_ws, which lets
+        steps with few rows of work split their key ranges over more
+        workgroups (None: rba_fwd_step / rba_fwd_step_acc, never split)."""
+        self.workspace = workspace
         self.w = w
         self.r = w.rank if rank is None else rank
         self.device = torch.device(device)
@@ -126,8 +131,20 @@ class RingReplay:
     def fwd_step(self, i: int, into_acc: bool, stream=None) -> int:
         s = self.steps[i]
         o, l = (self.o_acc, self.lse_acc) if into_acc else (self.o_part, self.lse_part)
+        if self.workspace is not None:
+            return rba.rba_fwd_step_ws(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                       self.kv_segs[s.src], o, l, False, None, rba.RBA_BF16, self.workspace, stream)
         return rba.rba_fwd_step(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
                                 self.kv_segs[s.src], o, l, stream)
+
+    def fwd_step_acc(self, i: int, o_final=None, final_dtype: int = rba.RBA_BF16, stream=None) -> int:
+        s = self.steps[i]
+        if self.workspace is not None:
+            return rba.rba_fwd_step_ws(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                       self.kv_segs[s.src], self.o_acc, self.lse_acc, True, o_final, final_dtype,
+                                       self.workspace, stream)
+        return rba.rba_fwd_step_acc(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
+                                    self.kv_segs[s.src], self.o_acc, self.lse_acc, o_final, final_dtype, stream)
 
     def forward(self, stream=None, on_step=None, fused_merge: bool = True, resume: bool = False) -> torch.Tensor:
         """Replay all steps; returns o_final (merged output in the input dtype).
@@ -160,10 +177,7 @@ class RingReplay:
             if first or not fused_merge:
                 st = self.fwd_step(i, into_acc=first, stream=stream)
             else:
-                s = self.steps[i]
-                st = rba.rba_fwd_step_acc(self.attn, self.q, self.q_segs, self.k[s.src], self.v[s.src],
-                                          self.kv_segs[s.src], self.o_acc, self.lse_acc,
-                                          self.o_final if last else None, final_dtype, stream)
+                st = self.fwd_step_acc(i, self.o_final if last else None, final_dtype, stream)
             assert st == rba.RBA_OK, "host plan and step status disagree"
             if not first and not fused_merge:
                 if on_step:

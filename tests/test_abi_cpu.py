@@ -343,3 +343,58 @@ def test_merge_thread_map_keeps_each_pair_in_one_wave():
             vecs = sorted(covered[("vec", slot)])
             assert vecs == list(range(nv)), f"d={d}: pair slot {slot} vectors {vecs[:8]}..."
 
+
+def test_probe_library_exports_its_header():
+    """librba_probe.so (the benchmark's measurement probes) exports every
+    entry point include/rba_probe.h declares, and rejects bad arguments
+    before any launch."""
+    from ring_sequence_parallelism_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rba_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(rba_[a-z_0-9]+)\s*\(", text)))
+    assert set(names) == set(probe.EXPORTS)
+    lib = probe.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    fl = ctypes.c_double(0)
+    assert lib.rba_probe_mfma_bf16(0, 10, FAKE, ctypes.byref(fl), None) == rba.RBA_ERR_INVALID
+    assert lib.rba_probe_mfma_bf16(4, 0, FAKE, ctypes.byref(fl), None) == rba.RBA_ERR_INVALID
+    assert lib.rba_probe_copy(FAKE, FAKE, 64, 4, None) == rba.RBA_ERR_INVALID          # overlap
+    assert lib.rba_probe_copy(FAKE, ctypes.c_void_p(1 << 40), 20, 4, None) == rba.RBA_ERR_INVALID   # not x16
+
+
+def test_fwd_workspace_size_of_the_packed_document_steps():
+    """The host's split plan for the 64K packed-document replay: the steps
+    with few rows of work ask for a workspace, never more than 32 MiB; steps
+    that already fill the chip ask for none; empty steps report
+    RBA_STEP_EMPTY.  Host only (the compute-unit count of a missing device
+    reads as 256)."""
+    w = W.WORKLOADS["c3"]
+    cu = W.gen_cu_seqlens(w)
+    a = rba.attn_params(w.hq, w.hkv, w.d, w.scale, rba.RBA_BF16, rba.RBA_MASK_DOC_CAUSAL, None, cu)
+    a.cu_seqlens_dev = 0x10000
+    lib = rba.load()
+    sizes = {}
+    for r in range(w.n_ranks):
+        for s in range(w.n_ranks):
+            j = (r - s) % w.n_ranks
+            qs, ks = rba.make_segs(w.rank_runs(r)), rba.make_segs(w.rank_runs(j))
+            n = ctypes.c_int64(-1)
+            rc = lib.rba_fwd_workspace_size(ctypes.byref(a), 4096, ctypes.byref(qs), 4096, ctypes.byref(ks),
+                                            ctypes.byref(n))
+            st, pairs = rba.rba_plan_step(a, 4096, qs, 4096, ks)
+            assert rc == st
+            if st == rba.RBA_STEP_EMPTY:
+                assert n.value == 0
+                continue
+            assert 0 <= n.value <= 32 << 20
+            sizes[(r, j)] = (n.value, pairs)
+    assert any(b > 0 for b, _ in sizes.values())
+    # the whole 4096 x 4096 block of one long document fills the chip: no split
+    full = [b for (b, p) in sizes.values() if p == 4096 * 4096]
+    assert full and all(b == 0 for b in full)
+    # fp32 steps never split
+    a32 = rba.attn_params(2, 2, 64, 0.125, rba.RBA_F32, rba.RBA_MASK_NONE)
+    n = ctypes.c_int64(-1)
+    assert lib.rba_fwd_workspace_size(ctypes.byref(a32), 64, ctypes.byref(rba.make_segs([(0, 64)])), 4096,
+                                      ctypes.byref(rba.make_segs([(0, 4096)])), ctypes.byref(n)) == rba.RBA_OK
+    assert n.value == 0
