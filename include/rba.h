@@ -180,6 +180,34 @@ int rba_fwd_step_ws(const rba_attn* a,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * rba_fwd_step_noalloc — rba_fwd_step_ws with the workspace in a fixed
+ * device array of the library instead of caller memory.  For callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the call allocates and
+ * frees nothing, and calls no allocating library routine.
+ *   The array is 32 MiB (the most any split plan of rba_fwd_step_ws uses;
+ *   a launch that would need more takes fewer, longer items or runs
+ *   unsplit, and a plan over 32 MiB would be refused with RBA_ERR_INVALID).
+ *   Each device holds its own copy from the first call on it until the
+ *   process ends; the first call on a device, with that device current,
+ *   looks up the copy's address (hipGetSymbolAddress) and keeps it.
+ *   Every call on one device shares that device's array and leaves the last
+ *   split's partials in it; no part of it needs to start at zero (a split's
+ *   merge reads only slots its own first launch wrote).  Calls that overlap
+ *   on one device (other streams, other threads) race on the array and must
+ *   be serialised by the caller.
+ * Arguments, results, limits, errors and RBA_STEP_EMPTY behaviour as
+ * rba_fwd_step_ws with workspace = the array; results are bit for bit those
+ * of rba_fwd_step_ws given a 32 MiB workspace.  Devices 64 and above are
+ * RBA_ERR_UNSUPPORTED.
+ */
+int rba_fwd_step_noalloc(const rba_attn* a,
+                         const void* q, int64_t sq, const rba_segs* q_segs,
+                         const void* k, const void* v, int64_t sk, const rba_segs* kv_segs,
+                         float* o, float* lse, int32_t accumulate, void* o_final, int32_t final_dtype,
+                         void* stream);
+
+/*
  * rba_fwd_workspace_size — host-side query (reads the current device's
  * compute-unit count, launches nothing): *bytes = the workspace
  * rba_fwd_step_ws would use for this step (0 when it would not split), at

@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -516,12 +517,53 @@ int64_t plan_split(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fwd
   }
 }
 
+// Workspace of rba_fwd_step_noalloc: the split partials of one forward
+// step, in a fixed device array instead of caller memory.  Each device the
+// library runs on holds its own copy for the life of the process.  In host
+// code `scratch` names a host-side stand-in, never the device array: kernels
+// and copies get the per-device address from scratch_address().
+constexpr int64_t kScratchBytes = kSplitMaxBytes;
+constexpr int kMaxScratchDevices = 64;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the device is current during the lookup) and kept.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RBA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(RBA_ERR_UNSUPPORTED, "device %d: the no-allocation workspace serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RBA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RBA_OK;
+}
+
 // Shared body of the forward entry points: the partial written to o / lse,
 // or merged into the running o / lse (accumulate); with a workspace of
-// ws_bytes bytes a launch with too few workgroups may be split (plan_split).
+// ws_bytes bytes (or, with use_scratch, the device's `scratch` array) a
+// launch with too few workgroups may be split (plan_split).
 int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k, const void* v,
              int64_t sk, const rba_segs* kv_segs, float* o, float* lse, bool accumulate, void* o_final,
-             int32_t final_dtype, void* stream, void* ws = nullptr, int64_t ws_bytes = 0) {
+             int32_t final_dtype, void* stream, void* ws = nullptr, int64_t ws_bytes = 0,
+             bool use_scratch = false) {
   g_err.clear();
   StepPlan plan;
   int rc = prepare_step(a, sq, q_segs, sk, kv_segs, false, plan);
@@ -547,10 +589,18 @@ int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
   p.o_final = o_final;
   p.final_bf16 = final_dtype == RBA_BF16;
   if ((rc = fill_query_tiling(a, sq, sk, plan, rba::fwd_rows_per_wave(a->d, bf16), p))) return rc;
+  if (use_scratch) {
+    if ((rc = scratch_address(&ws))) return rc;
+    ws_bytes = kScratchBytes;
+  }
   if (ws) {
     if ((rc = check_ptr(ws, "workspace"))) return rc;
     if (ws_bytes < 0) return fail(RBA_ERR_INVALID, "negative workspace size");
-    if (plan_split(a, plan, sq, p, ws_bytes) > 0) p.ws = static_cast<float*>(ws);
+    const int64_t need = plan_split(a, plan, sq, p, ws_bytes);
+    if (need > ws_bytes)
+      return fail(RBA_ERR_INVALID, "forward step: split plan needs %lld workspace bytes, %lld given",
+                  (long long)need, (long long)ws_bytes);
+    if (need > 0) p.ws = static_cast<float*>(ws);
   }
   hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
   if (e == hipSuccess && p.split) e = rba::launch_split_merge(p, a->d, (hipStream_t)stream);
@@ -619,6 +669,17 @@ int rba_fwd_step_ws(const rba_attn* a, const void* q, int64_t sq, const rba_segs
   }
   return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o, lse, accumulate != 0, o_final, final_dtype, stream,
                   workspace, workspace_bytes);
+}
+
+int rba_fwd_step_noalloc(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_segs, const void* k,
+                         const void* v, int64_t sk, const rba_segs* kv_segs, float* o, float* lse,
+                         int32_t accumulate, void* o_final, int32_t final_dtype, void* stream) {
+  if (!accumulate && o_final) {
+    g_err.clear();
+    return fail(RBA_ERR_INVALID, "o_final is written only when accumulating");
+  }
+  return fwd_step(a, q, sq, q_segs, k, v, sk, kv_segs, o, lse, accumulate != 0, o_final, final_dtype, stream,
+                  nullptr, 0, true);
 }
 
 int rba_merge(int64_t sq, int32_t hq, int32_t d, float* o_acc, float* lse_acc, const float* o_part,

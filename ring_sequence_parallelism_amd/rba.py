@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librba.so")
 
 EXPORTS = ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
            "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_fwd_step_ws", "rba_fwd_workspace_size",
-           "rba_last_error", "rba_version")
+           "rba_fwd_step_noalloc", "rba_last_error", "rba_version")
 
 
 class RbaError(RuntimeError):
@@ -102,8 +102,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.rba_merge_layout.argtypes = [I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.rba_fwd_step_ws.argtypes = [A, P, I64, S, P, P, I64, S, P, P, I32, P, I32, P, I64, P]
     lib.rba_fwd_workspace_size.argtypes = [A, I64, S, I64, S, ctypes.POINTER(I64)]
+    lib.rba_fwd_step_noalloc.argtypes = [A, P, I64, S, P, P, I64, S, P, P, I32, P, I32, P]
     for fn in ("rba_fwd_step", "rba_fwd_step_acc", "rba_merge", "rba_bwd_preprocess", "rba_bwd_step", "rba_bwd_step_acc",
-               "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_fwd_step_ws", "rba_fwd_workspace_size"):
+               "rba_plan_step", "rba_step_full_tiles", "rba_merge_layout", "rba_fwd_step_ws", "rba_fwd_workspace_size",
+               "rba_fwd_step_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.rba_last_error.restype = ctypes.c_char_p
     lib.rba_last_error.argtypes = []
@@ -170,6 +172,15 @@ def rba_fwd_step_ws(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, o
         ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
         ctypes.byref(kv_segs), _ptr(o), _ptr(lse), 1 if accumulate else 0, _ptr(o_final), final_dtype,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rba_fwd_step_noalloc(a: rba_attn, q, q_segs: rba_segs, k, v, kv_segs: rba_segs, o, lse, accumulate: bool,
+                         o_final=None, final_dtype: int = RBA_BF16, stream=None) -> int:
+    """rba_fwd_step_ws with the library's per-device workspace array."""
+    return _check("rba_fwd_step_noalloc", load().rba_fwd_step_noalloc(
+        ctypes.byref(a), _ptr(q), q.shape[0], ctypes.byref(q_segs), _ptr(k), _ptr(v), k.shape[0],
+        ctypes.byref(kv_segs), _ptr(o), _ptr(lse), 1 if accumulate else 0, _ptr(o_final), final_dtype,
+        _stream(stream)))
 
 
 def rba_fwd_workspace_size(a: rba_attn, sq: int, q_segs: rba_segs, sk: int, kv_segs: rba_segs) -> int:
