@@ -58,6 +58,17 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu, int32_t n_docs, in
   return cu[lo + 1];
 }
 
+// The same from the document table in registers (see DocLanes), for a
+// wave-uniform position and for a position per lane.
+__device__ __forceinline__ int32_t doc_end_u(const DocLanes& d, const int32_t* cu, int32_t n_docs, int32_t p) {
+  if (!d.ok) return doc_end(cu, n_docs, p);
+  return __builtin_amdgcn_readlane(d.v, doc_index_u(d, p) + 1);
+}
+__device__ __forceinline__ int32_t doc_end_v(const DocLanes& d, const int32_t* cu, int32_t n_docs, int32_t p) {
+  if (!d.ok) return doc_end(cu, n_docs, p);
+  return __shfl(d.v, doc_index_v(d, n_docs, p) + 1);
+}
+
 // Walks the 32-row query blocks whose positions fall in [q_lo, q_hi] (per
 // query segment, in row order, each block once).  All fields are
 // workgroup-uniform.
@@ -159,9 +170,26 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
   // query block in that range loads nothing (and, unless it must store its
   // zero gradients, writes nothing).
   const PosRange tkr = pos_range(p.ks, kr0, kr1);
+  const int my_krow = wk0 + col;
+  const int32_t my_kpos = (my_krow < p.sk && !FULL) ? row_to_pos(p.ks, my_krow) : INT32_MAX;
   int64_t q_lo = kPosNegInf, q_hi = kPosPosInf;
   if (p.mask != kMaskNone) q_lo = tkr.lo;
-  if (p.mask == kMaskDoc) q_hi = (int64_t)doc_end(p.cu, p.n_docs, tkr.hi) - 1;
+  // document ends (document mask): of the tile's last key, of this lane's
+  // key and of the wave's key range, all looked up before any tile load
+  int32_t my_kend = INT32_MAX, wkend_lo = INT32_MAX, wkend_hi = INT32_MAX;
+  if (p.mask == kMaskDoc) {
+    const DocLanes dl = doc_lanes(p.cu, p.n_docs, lane);
+    q_hi = (int64_t)doc_end_u(dl, p.cu, p.n_docs, tkr.hi) - 1;
+    if (!FULL) {
+      // every lane looks up (keys past the chunk: the tile's first key)
+      const int32_t e = doc_end_v(dl, p.cu, p.n_docs, my_krow < p.sk ? my_kpos : tkr.lo);
+      if (my_krow < p.sk) my_kend = e;
+      if (wave_any) {
+        wkend_lo = doc_end_u(dl, p.cu, p.n_docs, wkr.lo);
+        wkend_hi = doc_end_u(dl, p.cu, p.n_docs, wkr.hi);
+      }
+    }
+  }
   QIter first{-1, 0, 0, 0, 1};
   qiter_next(first, p, q_lo, q_hi);
   const bool stores = p.heads_per_wg == p.group && !p.accumulate;
@@ -181,17 +209,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     const bf16x8* src = reinterpret_cast<const bf16x8*>(vbase + ((size_t)krow * p.hkv + g) * D);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) vreg[ks] = src[2 * ks + half];
-  }
-  const int my_krow = wk0 + col;
-  const int32_t my_kpos = (my_krow < p.sk && !FULL) ? row_to_pos(p.ks, my_krow) : INT32_MAX;
-  // document ends (document mask): of this lane's key and of the wave's key range
-  int32_t my_kend = INT32_MAX, wkend_lo = INT32_MAX, wkend_hi = INT32_MAX;
-  if (!FULL && p.mask == kMaskDoc) {
-    if (my_krow < p.sk) my_kend = doc_end(p.cu, p.n_docs, my_kpos);
-    if (wave_any) {
-      wkend_lo = doc_end(p.cu, p.n_docs, wkr.lo);
-      wkend_hi = doc_end(p.cu, p.n_docs, wkr.hi);
-    }
   }
 
   f32x16 dkacc[D / 32], dvacc[D / 32];

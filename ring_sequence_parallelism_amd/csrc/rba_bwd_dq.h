@@ -70,7 +70,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
     }
   }
   const int32_t qpos = (row_ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
-  const int32_t qds = (row_ok && !FULL && p.mask == kMaskDoc) ? wave_doc_start(p, t, qpos) : INT32_MIN;
+  const int32_t qds = (row_ok && !FULL && p.mask == kMaskDoc) ? t.lane_ds : INT32_MIN;
   // LSE in base 2 (rows without any allowed key, LSE = -inf, get P = 0 like
   // rows past the chunk), and delta.
   float lse2 = INFINITY, dlt = 0.f;

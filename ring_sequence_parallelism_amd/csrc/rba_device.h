@@ -42,6 +42,55 @@ __device__ __forceinline__ int32_t doc_start(const int32_t* cu, int32_t n_docs, 
   return cu[lo];
 }
 
+// The document table in registers: lane l of a wave holds cu[l] for
+// l <= n_docs (INT32_MAX above), when the whole table fits one wave
+// (n_docs < 64).  A document lookup is then a compare and a ballot (or, for
+// a position per lane, a 6-step search over the lanes) instead of a chain
+// of dependent loads from global memory.  `ok` is wave-uniform; without it
+// the lookups fall back to the binary search over cu.  Every lane of the
+// wave must take part in the lookups (they read other lanes' entries).
+struct DocLanes {
+  int32_t v;
+  bool ok;
+};
+
+__device__ __forceinline__ DocLanes doc_lanes(const int32_t* cu, int32_t n_docs, int lane) {
+  DocLanes d;
+  d.ok = cu != nullptr && n_docs > 0 && n_docs < 64;
+  d.v = (d.ok && lane <= n_docs) ? cu[lane] : INT32_MAX;
+  return d;
+}
+
+// Index t < n_docs of the document holding the wave-uniform position p (the
+// largest t with cu[t] <= p): the entries <= p form a prefix of the lanes.
+__device__ __forceinline__ int doc_index_u(const DocLanes& d, int32_t p) {
+  return __popcll(__ballot(d.v <= p)) - 1;
+}
+
+// The same for a position per lane: binary search over the lanes' entries.
+__device__ __forceinline__ int doc_index_v(const DocLanes& d, int32_t n_docs, int32_t p) {
+  int lo = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+    const int cand = lo + step;
+    const int32_t c = __shfl(d.v, min(cand, 63));
+    if (cand < n_docs && c <= p) lo = cand;
+  }
+  return lo;
+}
+
+// Document start of a wave-uniform position p (any n_docs).
+__device__ __forceinline__ int32_t doc_start_u(const DocLanes& d, const int32_t* cu, int32_t n_docs, int32_t p) {
+  if (!d.ok) return doc_start(cu, n_docs, p);
+  return __builtin_amdgcn_readlane(d.v, doc_index_u(d, p));
+}
+
+// Document start of a position per lane (any n_docs).
+__device__ __forceinline__ int32_t doc_start_v(const DocLanes& d, const int32_t* cu, int32_t n_docs, int32_t p) {
+  if (!d.ok) return doc_start(cu, n_docs, p);
+  return __shfl(d.v, doc_index_v(d, n_docs, p));
+}
+
 // Minimum and maximum global position over chunk rows [r0, r1) (r0 < r1),
 // and whether those rows lie in a single segment (then row r0 + i is at
 // position lo + i * stride).

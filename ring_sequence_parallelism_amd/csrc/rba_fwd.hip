@@ -81,7 +81,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       qreg[qb][ks] = ok ? src[2 * ks + half] : z;
     }
     qpos[qb] = (ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
-    qds[qb] = (ok && !FULL && p.mask == kMaskDoc) ? wave_doc_start(p, t, qpos[qb]) : INT32_MIN;
+    // the lane's own row's document start comes with the task (NQB = 1)
+    const int32_t ds = qb == 0 ? t.lane_ds : wave_doc_start(p, t, qpos[qb]);
+    qds[qb] = (ok && !FULL && p.mask == kMaskDoc) ? ds : INT32_MIN;
   }
 
   const KvLoader<D> loader(p, t.g, wave, lane, lds_addr(&lds[0][0][0]));
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
     for (int ks = 0; ks < D / 2; ++ks) qreg[ks] = row_ok ? src[2 * ks + half] : 0.f;
   }
   const int32_t qpos = row_ok ? row_to_pos(p.qs, row) : kPosNone;
-  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? wave_doc_start(p, t, qpos) : INT32_MIN;
+  const int32_t qds = (row_ok && p.mask == kMaskDoc) ? t.lane_ds : INT32_MIN;
 
   f32x16 oacc[D / 32];
 #pragma unroll

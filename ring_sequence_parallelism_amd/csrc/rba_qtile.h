@@ -26,6 +26,9 @@ struct WaveTask {
   // count) of its row group and writes its partial to workspace slot `slot`
   // (-1: the whole visit list, written to the output)
   int skip, count, slot;
+  // document mask: start of the document of this lane's row (row0 + lane %
+  // 32), INT32_MIN for rows past the chunk and other masks
+  int32_t lane_ds;
 };
 
 template <int QR>
@@ -76,18 +79,30 @@ __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int 
   const int wr1 = min(t.row0 + QR, p.sq);
   t.wave_any = t.row0 < wr1;
   t.wq_lo = INT32_MAX; t.wq_hi = INT32_MIN; t.wds_lo = INT32_MIN; t.wds_hi = INT32_MIN;
+  t.lane_ds = INT32_MIN;
   if (t.wave_any) {
     PosRange r = pos_range(p.qs, t.row0, wr1);
     t.wq_lo = r.lo; t.wq_hi = r.hi;
-    if (p.mask == kMaskDoc) {
-      t.wds_lo = doc_start(p.cu, p.n_docs, r.lo);
-      t.wds_hi = doc_start(p.cu, p.n_docs, r.hi);
-    }
   }
   PosRange wr = pos_range(p.qs, t.wg_row0, t.wg_row0 + t.wg_rows);
   t.k_lo = kPosNegInf; t.k_hi = kPosPosInf;
   if (p.mask != kMaskNone) t.k_hi = wr.hi;
-  if (p.mask == kMaskDoc) t.k_lo = doc_start(p.cu, p.n_docs, wr.lo);
+  if (p.mask == kMaskDoc) {
+    // every document lookup of the task, from the table in registers
+    const DocLanes dl = doc_lanes(p.cu, p.n_docs, threadIdx.x & 63);
+    t.k_lo = doc_start_u(dl, p.cu, p.n_docs, wr.lo);
+    if (t.wave_any) {
+      t.wds_lo = doc_start_u(dl, p.cu, p.n_docs, t.wq_lo);
+      t.wds_hi = doc_start_u(dl, p.cu, p.n_docs, t.wq_hi);
+      // the lane's row (rows past the chunk look up the wave's first position)
+      const int row = t.row0 + (int)(threadIdx.x & 31);
+      const bool ok = row < p.sq;
+      const int32_t ds = t.wds_lo == t.wds_hi
+                             ? t.wds_lo
+                             : doc_start_v(dl, p.cu, p.n_docs, ok ? row_to_pos(p.qs, row) : t.wq_lo);
+      t.lane_ds = ok ? ds : INT32_MIN;
+    }
+  }
   return t;
 }
 
