@@ -55,7 +55,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
   const int col = lane & 31, half = lane >> 5;
-  const WaveTask t = make_task<QR>(p, wave, blockIdx.x);
+  const int logical = xcd_remap(blockIdx.x, p.n_wg);
+  // A merging step leaves the running result of rows that see no key as it
+  // is (an empty partial merges as the identity): workgroups the host has
+  // listed after every row group with work end at once.
+  if (!p.split && p.n_order && p.accumulate && !p.o_final && logical % p.n_row_groups >= p.n_active) return;
+  const TaskHead th = task_head(p, logical);
+
+  // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
+  // Loaded first, so that the rest of the task setup runs while it lands.
+  bf16x8 qreg[NQB][D / 16];
+  {
+    const int row0 = task_row0<QR>(p, th, wave), h = task_head_index(p, th, wave);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = row0 + qb * 32 + col;
+      const bool ok = row < p.sq;
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(
+          static_cast<const uint16_t*>(p.q) + ((size_t)(ok ? row : 0) * p.hq + h) * D);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 z = {};
+        qreg[qb][ks] = ok ? src[2 * ks + half] : z;
+      }
+    }
+  }
+  const WaveTask t = make_task_from<QR>(p, wave, th);
   TileIter it{-1, 0, 0, 0, 1};
   tile_next(it, p, t);
   // a split item starts t.skip tiles into its row group's visit list and
@@ -66,20 +91,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // it is (an empty partial merges as the identity).
   if (!it.valid && t.slot < 0 && p.accumulate && !p.o_final) return;
 
-  // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
-  bf16x8 qreg[NQB][D / 16];
   int32_t qpos[NQB], qds[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int row = t.row0 + qb * 32 + col;
     const bool ok = row < p.sq;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(
-        static_cast<const uint16_t*>(p.q) + ((size_t)(ok ? row : 0) * p.hq + t.h) * D);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 z = {};
-      qreg[qb][ks] = ok ? src[2 * ks + half] : z;
-    }
     qpos[qb] = (ok && !FULL) ? row_to_pos(p.qs, row) : kPosNone;
     // the lane's own row's document start comes with the task (NQB = 1)
     const int32_t ds = qb == 0 ? t.lane_ds : wave_doc_start(p, t, qpos[qb]);

@@ -327,6 +327,7 @@ int64_t host_doc_start(const DocTable& dt, int64_t p) {
 void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::FwdParams& p, int64_t rows_per_wg) {
   p.n_order = 0;
   p.order_reverse = 0;
+  p.n_active = p.n_row_groups;
   if (a->mask == RBA_MASK_NONE) return;
   if (a->mask == RBA_MASK_DOC_CAUSAL && !plan.dt.cu) return;
   std::vector<std::pair<int64_t, int>> work(p.n_row_groups);
@@ -359,6 +360,10 @@ void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fw
   });
   for (int i = 0; i < p.n_row_groups; ++i) p.order[i] = (uint16_t)work[i].second;
   p.n_order = p.n_row_groups;
+  // the row groups with work come first; the others visit no key tile
+  int n_active = 0;
+  while (n_active < p.n_row_groups && work[n_active].first > 0) ++n_active;
+  p.n_active = n_active;
 }
 
 // Does every key tile that a query-stationary workgroup visits hold only

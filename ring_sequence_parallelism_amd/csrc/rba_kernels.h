@@ -70,6 +70,9 @@ struct FwdParams {
   // groups are one item each, numbered after the split ones, and write the
   // output directly; row groups without work follow (one workgroup each).
   int32_t split;
+  // Row groups with work (the first n_active of `order` when it is given;
+  // set for unsplit launches too, where the rest end at once in a merging
+  // step).
   int32_t n_active;
   int32_t n_split_rg;
   int32_t n_items;        // items of the n_active row groups

@@ -31,10 +31,17 @@ struct WaveTask {
   int32_t lane_ds;
 };
 
-template <int QR>
-__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int block) {
-  const int logical = xcd_remap(block, p.n_wg);
-  WaveTask t;
+// Which head group and row group a workgroup works on, and for a split
+// item the run of tiles and the workspace slot: the first, cheap part of
+// the task (no position ranges, no document lookups), enough to address
+// the workgroup's query rows.
+struct TaskHead {
+  int hg, rg;
+  int skip, count, slot;
+};
+
+__device__ __forceinline__ TaskHead task_head(const FwdParams& p, int logical) {
+  TaskHead t;
   t.skip = 0;
   t.count = INT32_MAX;
   t.slot = -1;
@@ -70,6 +77,28 @@ __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int 
     rg = p.order[i];
   }
   t.hg = hg;
+  t.rg = rg;
+  return t;
+}
+
+// First query row and query head of a wave of the task.
+template <int QR>
+__device__ __forceinline__ int task_row0(const FwdParams& p, const TaskHead& th, int wave) {
+  return th.rg * p.rbw * QR + (wave / p.hpw) * QR;
+}
+__device__ __forceinline__ int task_head_index(const FwdParams& p, const TaskHead& th, int wave) {
+  return th.hg * p.hpw + wave % p.hpw;
+}
+
+// The rest of the task: row and key position ranges, document starts.
+template <int QR>
+__device__ __forceinline__ WaveTask make_task_from(const FwdParams& p, int wave, const TaskHead& th) {
+  WaveTask t;
+  t.skip = th.skip;
+  t.count = th.count;
+  t.slot = th.slot;
+  const int hg = th.hg, rg = th.rg;
+  t.hg = hg;
   const int hw = wave % p.hpw, rb = wave / p.hpw;
   t.h = hg * p.hpw + hw;
   t.g = t.h / p.group;
@@ -104,6 +133,11 @@ __device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int 
     }
   }
   return t;
+}
+
+template <int QR>
+__device__ __forceinline__ WaveTask make_task(const FwdParams& p, int wave, int block) {
+  return make_task_from<QR>(p, wave, task_head(p, xcd_remap(block, p.n_wg)));
 }
 
 // Document start of a query row at position qpos of the wave: the wave's
