@@ -42,8 +42,12 @@
  *   - All arguments are validated before anything is launched.  On any
  *     negative status nothing was launched and no output was touched; the
  *     reason is in rba_last_error().
- *   - The library is stateless apart from a thread-local error string and is
- *     safe to call from several threads on different streams.
+ *   - The library keeps no state between calls apart from a thread-local
+ *     error string, per-device caches of the device's architecture and
+ *     compute-unit count, and the per-device workspace array of
+ *     rba_fwd_step_noalloc.  It is safe to call from several threads on
+ *     different streams, except rba_fwd_step_noalloc calls that overlap on
+ *     one device (see there).
  */
 #ifndef RBA_H
 #define RBA_H

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -228,34 +229,38 @@ int check_ptr(const void* p, const char* what) {
   return RBA_OK;
 }
 
-// gfx950 check, cached per device.
+// gfx950 check, cached per device (devices 0..63; others are checked on
+// every call).  The caches are atomics: calls from several host threads
+// may fill them at once, with the same values.
 int check_device() {
-  static int state[64] = {0};  // 0 unknown, 1 ok, -1 unsupported
+  static std::atomic<int> state[64];  // 0 unknown, 1 ok, -1 unsupported
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(RBA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= 64) return RBA_OK;
-  if (state[dev] == 0) {
+  const bool cached = dev >= 0 && dev < 64;
+  int st = cached ? state[dev].load(std::memory_order_relaxed) : 0;
+  if (st == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(RBA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-    state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (cached) state[dev].store(st, std::memory_order_relaxed);
   }
-  if (state[dev] < 0) return fail(RBA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (st < 0) return fail(RBA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
   return RBA_OK;
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 int hip_status(hipError_t e, const char* what) {

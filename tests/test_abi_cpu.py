@@ -398,3 +398,35 @@ def test_fwd_workspace_size_of_the_packed_document_steps():
     assert lib.rba_fwd_workspace_size(ctypes.byref(a32), 64, ctypes.byref(rba.make_segs([(0, 64)])), 4096,
                                       ctypes.byref(rba.make_segs([(0, 4096)])), ctypes.byref(n)) == rba.RBA_OK
     assert n.value == 0
+
+
+def test_host_calls_from_several_threads():
+    """The planner and the error string are per call / per thread: several
+    host threads planning steps at once get each their own pair counts, and
+    a thread's error text is not overwritten by another thread's calls."""
+    import threading
+    lib = rba.load()
+    errors, results = [], {}
+
+    def worker(i):
+        try:
+            a = _attn(mask=rba.RBA_MASK_CAUSAL)
+            for rep in range(200):
+                n = 64 + i
+                st, pairs = rba.rba_plan_step(a, n, rba.make_segs([(0, n)]), n, rba.make_segs([(0, n)]))
+                assert st == rba.RBA_OK and pairs == n * (n + 1) // 2
+                bad = _attn(d=96)   # rejected: unsupported head dimension
+                assert _fwd(bad, 64, SEG64, 64, SEG64) == rba.RBA_ERR_UNSUPPORTED
+                msg = lib.rba_last_error().decode()
+                assert "96" in msg, msg
+            results[i] = True
+        except Exception as e:   # collected and re-raised in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[0]
+    assert len(results) == 8
