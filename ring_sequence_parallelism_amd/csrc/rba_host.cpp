@@ -423,6 +423,7 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   const int64_t rows_per_wg = query_rows_per_wg(p.group, rows_per_wave);
   p.n_row_groups = (int32_t)((sq + rows_per_wg - 1) / rows_per_wg);
   p.n_head_groups = a->hq / p.hpw;
+  p.n_rg_launch = p.n_row_groups;
   const int64_t n_wg = (int64_t)p.n_row_groups * p.n_head_groups;
   if (n_wg > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "too many workgroups");
   p.n_wg = (int32_t)n_wg;
@@ -611,6 +612,12 @@ int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
       return fail(RBA_ERR_INVALID, "forward step: split plan needs %lld workspace bytes, %lld given",
                   (long long)need, (long long)ws_bytes);
     if (need > 0) p.ws = static_cast<float*>(ws);
+  }
+  // A merging step launches no workgroup for the row groups listed after
+  // every one with work: they have no key to merge.
+  if (!p.split && p.n_order && accumulate && !o_final && p.n_active < p.n_row_groups) {
+    p.n_rg_launch = p.n_active;
+    p.n_wg = p.n_head_groups * p.n_active;
   }
   hipError_t e = bf16 ? rba::launch_fwd_bf16(p, a->d, (hipStream_t)stream) : rba::launch_fwd_f32(p, a->d, (hipStream_t)stream);
   if (e == hipSuccess && p.split) e = rba::launch_split_merge(p, a->d, (hipStream_t)stream);

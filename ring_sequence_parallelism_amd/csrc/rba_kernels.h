@@ -44,6 +44,10 @@ struct FwdParams {
   int32_t hpw;         // query heads per workgroup (1, 2 or 4)
   int32_t rbw;         // row blocks per workgroup (4 / hpw)
   int32_t n_row_groups;
+  // Row groups per head group that get a workgroup (unsplit launches): all
+  // of them, or in a merging step with the heavy-first order only the first
+  // n_active (the others have no key to merge).
+  int32_t n_rg_launch;
   int32_t n_head_groups;   // hq / hpw
   int32_t n_wg;
   // Heavy-first order of the row groups (host-computed from the masks and

@@ -47,8 +47,8 @@ __device__ __forceinline__ TaskHead task_head(const FwdParams& p, int logical) {
   t.slot = -1;
   int hg, rg;
   if (!p.split) {
-    hg = logical / p.n_row_groups;      // head group (query heads hg*hpw ...)
-    const int rg_i = logical % p.n_row_groups;
+    hg = logical / p.n_rg_launch;       // head group (query heads hg*hpw ...)
+    const int rg_i = logical % p.n_rg_launch;
     rg = p.n_order ? (int)p.order[rg_i]
                    : (p.order_reverse ? p.n_row_groups - 1 - rg_i : rg_i);   // heavy first when ordered
   } else {
