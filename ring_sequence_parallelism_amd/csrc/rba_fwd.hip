@@ -59,7 +59,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // A merging step leaves the running result of rows that see no key as it
   // is (an empty partial merges as the identity): workgroups the host has
   // listed after every row group with work end at once.
-  if (!p.split && p.n_order && p.accumulate && !p.o_final && logical % p.n_rg_launch >= p.n_active) return;
+  if (!p.split && (p.n_order || p.order_reverse) && p.accumulate && !p.o_final &&
+      logical % p.n_rg_launch >= p.n_active)
+    return;
   const TaskHead th = task_head(p, logical);
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.

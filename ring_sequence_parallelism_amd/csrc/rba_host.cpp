@@ -358,6 +358,12 @@ void fill_row_order(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fw
       equal = equal && work[rg].first == work[0].first;
     }
     p.order_reverse = (rising && !equal) ? 1 : 0;
+    if (p.order_reverse) {
+      // the row groups with work are a suffix, taken first
+      int n_active = 0;
+      while (n_active < p.n_row_groups && work[p.n_row_groups - 1 - n_active].first > 0) ++n_active;
+      p.n_active = n_active;
+    }
     return;
   }
   std::stable_sort(work.begin(), work.end(), [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
@@ -615,7 +621,7 @@ int fwd_step(const rba_attn* a, const void* q, int64_t sq, const rba_segs* q_seg
   }
   // A merging step launches no workgroup for the row groups listed after
   // every one with work: they have no key to merge.
-  if (!p.split && p.n_order && accumulate && !o_final && p.n_active < p.n_row_groups) {
+  if (!p.split && (p.n_order || p.order_reverse) && accumulate && !o_final && p.n_active < p.n_row_groups) {
     p.n_rg_launch = p.n_active;
     p.n_wg = p.n_head_groups * p.n_active;
   }

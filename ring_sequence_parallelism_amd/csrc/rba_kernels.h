@@ -45,8 +45,9 @@ struct FwdParams {
   int32_t rbw;         // row blocks per workgroup (4 / hpw)
   int32_t n_row_groups;
   // Row groups per head group that get a workgroup (unsplit launches): all
-  // of them, or in a merging step with the heavy-first order only the first
-  // n_active (the others have no key to merge).
+  // of them, or in a merging step with a heavy-first order (`order` or
+  // `order_reverse`) only the first n_active (the others have no key to
+  // merge).
   int32_t n_rg_launch;
   int32_t n_head_groups;   // hq / hpw
   int32_t n_wg;
