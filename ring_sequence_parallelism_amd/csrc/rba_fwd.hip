@@ -195,14 +195,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         // The tile maximum is compared in raw score units; it is scaled only
-        // when the running maximum moves.
+        // when the running maximum moves.  Both lanes of a query share its
+        // threshold, so each tests its own 32 of the tile's 64 keys; the two
+        // are combined only when the maximum moves.
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][qb][j]);
-        mx = half_max(mx);
         if (__any(mx > thr_raw[qb])) {
+          mx = half_max(mx);
           const float m_new = fmaxf(m_run[qb], mx * p.scale_log2);
           const float alpha = fast_exp2(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
           m_run[qb] = m_new;
