@@ -40,6 +40,9 @@
 
 namespace rba {
 
+// floor(a / b) for b > 0.
+__device__ __forceinline__ int floor_div_i32(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
 // FULL: every visited tile is full for every wave (shown on the host), so
 // the tile body has no classification and no mask code.
 template <int D, int NQB, bool FULL>
@@ -123,6 +126,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 
   if (it.valid) loader.issue(it.kt, 0);
+  // With one contiguous KV run, the key tiles that are full for this wave
+  // (every key at or before its first row, at or after the latest document
+  // start of its rows, inside the chunk) are the tile indices [f_lo, f_hi].
+  bool iv = false;
+  int f_lo = 1, f_hi = 0;
+  if (!FULL && p.ks.n == 1 && p.ks.stride[0] == 1) {
+    iv = true;
+    if (t.wave_any) {
+      const int32_t st = p.ks.start[0];          // position of key row 0
+      int lo = 0, hi = p.sk / kBN - 1;          // tiles not past the chunk
+      if (p.mask != kMaskNone) hi = min(hi, floor_div_i32(t.wq_lo - st - (kBN - 1), kBN));
+      if (p.mask == kMaskDoc) lo = max(lo, -floor_div_i32(st - t.wds_hi, kBN));
+      f_lo = lo;
+      f_hi = hi;
+    }
+  }
   // The body of one key tile, for a compile-time buffer index (the loop is
   // unrolled by two so LDS addresses of either buffer are immediate offsets).
   auto tile = [&](auto buf_c) {
@@ -144,9 +163,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     PosRange kr{0, 0, true, 1};
     int cls = kFull;
     if (!FULL) {
-      kr = tile_pos_range(it, p.ks, kr0, kr1);
-      const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
-      cls = cls0 == kSkip ? kPartial : cls0;
+      if (iv) {
+        cls = (kt >= f_lo && kt <= f_hi) ? kFull : kPartial;
+      } else {
+        kr = tile_pos_range(it, p.ks, kr0, kr1);
+        const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
+        cls = cls0 == kSkip ? kPartial : cls0;
+      }
     }
     {
       const char* kt_lds = lds[buf][0];
@@ -182,6 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       }
 
       if (!FULL && cls == kPartial) {
+        if (iv) kr = tile_pos_range(it, p.ks, kr0, kr1);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
