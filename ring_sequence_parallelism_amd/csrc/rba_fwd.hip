@@ -44,8 +44,10 @@ namespace rba {
 __device__ __forceinline__ int floor_div_i32(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
 // FULL: every visited tile is full for every wave (shown on the host), so
-// the tile body has no classification and no mask code.
-template <int D, int NQB, bool FULL>
+// the tile body has no classification and no mask code.  ONESEG: no key tile
+// spans two KV segments (every segment boundary on a tile boundary, shown on
+// the host), so the masked path has no per-element segment search.
+template <int D, int NQB, bool FULL, bool ONESEG>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int QR = 32 * NQB;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       if (iv) {
         cls = (kt >= f_lo && kt <= f_hi) ? kFull : kPartial;
       } else {
-        kr = tile_pos_range(it, p.ks, kr0, kr1);
+        kr = tile_pos_range<ONESEG>(it, p.ks, kr0, kr1);
         const int cls0 = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
         cls = cls0 == kSkip ? kPartial : cls0;
       }
@@ -205,11 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       }
 
       if (!FULL && cls == kPartial) {
-        if (iv) kr = tile_pos_range(it, p.ks, kr0, kr1);
+        if (iv) kr = tile_pos_range<ONESEG>(it, p.ks, kr0, kr1);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) mask_block(sacc[kb][qb], p, kr, kr0, kb, half, qpos[qb], qds[qb]);
+          for (int qb = 0; qb < NQB; ++qb) mask_block<ONESEG>(sacc[kb][qb], p, kr, kr0, kb, half, qpos[qb], qds[qb]);
       }
 
       // Online softmax (base 2) per query column with a lazy maximum: the
@@ -520,13 +522,17 @@ int fwd_rows_per_wave(int d, int dtype_bf16) {
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
   dim3 grid(p.n_wg), block(kThreads);
   if (d == 128 && p.all_full)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, true, true>), grid, block, 0, s, p);
+  else if (d == 128 && p.one_seg)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, false, true>), grid, block, 0, s, p);
   else if (d == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdNQB, false, false>), grid, block, 0, s, p);
   else if (d == 64 && p.all_full)
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, true, true>), grid, block, 0, s, p);
+  else if (d == 64 && p.one_seg)
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, false, true>), grid, block, 0, s, p);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdNQB, false, false>), grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

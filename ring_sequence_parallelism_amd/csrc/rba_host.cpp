@@ -435,6 +435,10 @@ int fill_query_tiling(const rba_attn* a, int64_t sq, int64_t sk, const StepPlan&
   p.n_wg = (int32_t)n_wg;
   fill_row_order(a, plan, sq, p, rows_per_wg);
   p.all_full = all_tiles_full(a, plan, sq, sk, rows_per_wg) ? 1 : 0;
+  // every KV segment boundary on a tile boundary: no tile spans two segments
+  p.one_seg = 1;
+  for (const Seg& k : plan.ks)
+    if (k.row0 % rba::kFwdTileKeys) p.one_seg = 0;
   return RBA_OK;
 }
 

@@ -63,6 +63,7 @@ struct FwdParams {
   // (no masked pair, inside the chunk, in one segment) for every wave of it,
   // so the kernel needs no tile classification and no per-element mask.
   int32_t all_full;
+  int32_t one_seg;    // no key tile spans two KV segments (launch choice)
   // Split key ranges (forward only; split = 0 elsewhere).  For a launch with
   // too few workgroups for the chip, `order` lists the row groups by
   // decreasing number of key tiles; the first n_active have work, and the

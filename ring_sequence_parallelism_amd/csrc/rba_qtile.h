@@ -203,8 +203,10 @@ __device__ __forceinline__ void tile_next(TileIter& it, const FwdParams& p, cons
 // Position range of key rows [r0, r1) of the tile the iterator is on: from
 // the current segment's fields when the rows lie inside it (the common case),
 // else from the segment table.
+// ONESEG: the caller knows that no key tile spans two KV segments.
+template <bool ONESEG = false>
 __device__ __forceinline__ PosRange tile_pos_range(const TileIter& it, const SegTable& t, int r0, int r1) {
-  if (r0 >= it.seg_r0 && r1 <= it.seg_r1)
+  if (ONESEG || (r0 >= it.seg_r0 && r1 <= it.seg_r1))
     return PosRange{it.seg_st + (r0 - it.seg_r0) * it.seg_sd, it.seg_st + (r1 - 1 - it.seg_r0) * it.seg_sd, true,
                     it.seg_sd};
   return pos_range(t, r0, r1);
@@ -266,7 +268,9 @@ struct KvLoader {
 // start qd) that the mask does not allow, or that lie past the chunk.  Lane
 // (col, half) holds keys kb * 32 + 8 * (j / 4) + 4 * half + j % 4 in element
 // j.  Every element is rewritten through a select (no conditional stores
-// into the vector).
+// into the vector).  ONESEG: no key tile spans two KV segments (kr.single
+// holds), so the per-element segment search is not compiled in.
+template <bool ONESEG = false>
 __device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const PosRange& kr, int kr0, int kb,
                                            int half, int32_t qpos, int32_t qd) {
   if (kr.single && kr.stride == 1) {
@@ -288,7 +292,7 @@ __device__ __forceinline__ void mask_block(f32x16& s, const FwdParams& p, const 
     return;
   }
   int32_t kp[16];
-  if (kr.single) {
+  if (ONESEG || kr.single) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) kp[j] = kr.lo + (kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3)) * kr.stride;
   } else {
