@@ -128,7 +128,7 @@ constexpr int dkdv_lds_bytes() { return kBK * D * 2 + 2 * 2 * kBQ * D * 2 + 2 * 
 // `smem` the workgroup's LDS (dkdv_lds_bytes<D>() bytes, 16-byte aligned).
 // FULL: every visited (key wave, query block) pair is full (shown on the
 // host), so blocks need no classification and no per-element mask.
-template <int D, bool FULL>
+template <int D, bool FULL, bool ONESEG = false>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* smem) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   constexpr int RB = D * 2;                  // bytes per tile row (swizzled, unpadded)
@@ -280,7 +280,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
     PosRange qr{0, 0, true, 1};
     int cls = wave_any ? kFull : kSkip;
     if (!FULL) {
-      qr = (qr0 >= it.seg_r0 && qr1 <= it.seg_r1)
+      qr = (ONESEG || (qr0 >= it.seg_r0 && qr1 <= it.seg_r1))
                ? PosRange{it.seg_st + (qr0 - it.seg_r0) * it.seg_sd,
                           it.seg_st + (qr1 - 1 - it.seg_r0) * it.seg_sd, true, it.seg_sd}
                : pos_range(p.qs, qr0, qr1);
@@ -322,7 +322,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int wg, char* 
             const int qrow = qr0 + qb0 + i;
             bool ok = my_krow < p.sk && qrow < p.sq;
             if (p.mask != kMaskNone) {
-              const int32_t qp = qr.single ? qr.lo + (qrow - qr0) * qr.stride : row_to_pos(p.qs, min(qrow, p.sq - 1));
+              const int32_t qp = (ONESEG || qr.single) ? qr.lo + (qrow - qr0) * qr.stride : row_to_pos(p.qs, min(qrow, p.sq - 1));
               ok = ok && my_kpos <= qp && qp < my_kend;
             }
             pv = ok ? pv : 0.f;
@@ -431,28 +431,35 @@ int bwd_keys_per_wg(int d) {
 // fills the CUs as the dK / dV tail drains.  The two passes share no output
 // and read the same inputs.  LDS is one buffer sized for the larger body.
 // FULL: both passes visit only full tiles / blocks (shown on the host).
-template <int D, bool FULL>
+template <int D, bool FULL, bool ONESEG>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kernel(BwdParams p, DqParams dp) {
   constexpr int SMEM = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int b = blockIdx.x;
   if (b < p.n_wg)
-    bwd_dkdv_body<D, FULL>(p, b, smem);
+    bwd_dkdv_body<D, FULL, ONESEG>(p, b, smem);
   else
-    bwd_dq_body<D, FULL>(dp, b - p.n_wg, smem);
+    bwd_dq_body<D, FULL, ONESEG>(dp, b - p.n_wg, smem);
 }
 
 hipError_t launch_bwd(const BwdParams& p, const DqParams& dp, int d, hipStream_t s) {
   dim3 grid(p.n_wg + dp.f.n_wg), block(kBwdThreads);
+  bool one_seg = dp.f.one_seg != 0;
+  for (int i = 1; i < p.qs.n; ++i)
+    if (p.qs.row0[i] % kBQ) one_seg = false;
   const bool full = p.all_full && dp.f.all_full;
   if (d == 128 && full)
-    hipLaunchKernelGGL((bwd_kernel<128, true>), grid, block, 0, s, p, dp);
+    hipLaunchKernelGGL((bwd_kernel<128, true, true>), grid, block, 0, s, p, dp);
+  else if (d == 128 && one_seg)
+    hipLaunchKernelGGL((bwd_kernel<128, false, true>), grid, block, 0, s, p, dp);
   else if (d == 128)
-    hipLaunchKernelGGL((bwd_kernel<128, false>), grid, block, 0, s, p, dp);
+    hipLaunchKernelGGL((bwd_kernel<128, false, false>), grid, block, 0, s, p, dp);
   else if (d == 64 && full)
-    hipLaunchKernelGGL((bwd_kernel<64, true>), grid, block, 0, s, p, dp);
+    hipLaunchKernelGGL((bwd_kernel<64, true, true>), grid, block, 0, s, p, dp);
+  else if (d == 64 && one_seg)
+    hipLaunchKernelGGL((bwd_kernel<64, false, true>), grid, block, 0, s, p, dp);
   else if (d == 64)
-    hipLaunchKernelGGL((bwd_kernel<64, false>), grid, block, 0, s, p, dp);
+    hipLaunchKernelGGL((bwd_kernel<64, false, false>), grid, block, 0, s, p, dp);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -36,7 +36,7 @@ constexpr int dq_lds_bytes() { return 2 * 2 * kBN * D * 2; }
 // `smem` the workgroup's LDS (dq_lds_bytes<D>() bytes, 16-byte aligned).
 // FULL: every visited tile is full for every wave (shown on the host), so
 // tiles need no classification and no mask.
-template <int D, bool FULL>
+template <int D, bool FULL, bool ONESEG = false>
 __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char* smem) {
   const FwdParams& p = dp.f;
   constexpr int CPR = D / 8;
@@ -107,7 +107,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
     PosRange kr{0, 0, true, 1};
     int cls = t.wave_any ? kFull : kSkip;
     if (!FULL) {
-      kr = tile_pos_range(it, p.ks, kr0, kr1);
+      kr = tile_pos_range<ONESEG>(it, p.ks, kr0, kr1);
       cls = classify(p.mask, kr, kr1 - kr0 < kBN, t.wq_lo, t.wq_hi, t.wds_lo, t.wds_hi, t.wave_any);
     }
     if (cls != kSkip) {
@@ -129,7 +129,7 @@ __device__ __forceinline__ void bwd_dq_body(const DqParams& dp, int block, char*
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], sacc, 0, 0, 0);
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dpacc, 0, 0, 0);
         }
-        if (!FULL && cls == kPartial) mask_block(sacc, p, kr, kr0, kb, half, qpos, qds);
+        if (!FULL && cls == kPartial) mask_block<ONESEG>(sacc, p, kr, kr0, kb, half, qpos, qds);
         // dS^T in place, packed to bf16 pairs in accumulator order.
         uint32_t w[8];
 #pragma unroll
