@@ -201,3 +201,84 @@ def test_random_forward_step_workspace(seed):
     mo, ml = oracle.merge(o0.astype(np.float64), l0.astype(np.float64), want_o, want_lse)
     assert_lse(lse_acc.cpu().numpy(), ml, "lse_acc")
     assert_close(o_acc.cpu().numpy(), mo, "bf16", "o_acc")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_ring_replay(seed):
+    """A ring of 2-5 KV chunks over random runs of one position range, taken
+    in a random order: the merged forward (running O and LSE, then the bf16
+    output) against attention over all the keys, and the backward steps'
+    dQ (accumulated over the ring) and per-chunk dK / dV against the whole
+    gradient.  A chunk may be empty for the mask (nothing launched)."""
+    rng = np.random.default_rng(20_000 + seed)
+    hq, hkv = HEADS[int(rng.integers(0, len(HEADS)))]
+    d = int(rng.choice([64, 128]))
+    mask = int(rng.integers(0, 3))
+    n_chunks = int(rng.integers(2, 6))
+    span = int(rng.integers(64, 600))
+    # cut [0, span) into runs and deal them out to the chunks (at most 8 runs each)
+    n_runs = int(rng.integers(n_chunks, min(span, 8 * n_chunks) + 1))
+    cuts = np.sort(rng.choice(np.arange(1, span), n_runs - 1, replace=False))
+    bounds = np.concatenate([[0], cuts, [span]])
+    owner = np.concatenate([rng.permutation(n_chunks), rng.integers(0, n_chunks, n_runs - n_chunks)])
+    chunks = [[(int(bounds[i]), int(bounds[i + 1] - bounds[i]))
+               for i in range(n_runs) if owner[i] == c] for c in range(n_chunks)]
+    sq = int(rng.integers(1, 201))
+    qsegs = _runs(rng, sq, int(rng.integers(0, span)))
+    qpos = _pos(qsegs)
+    cu = None
+    if mask == 2:
+        end = int(max(qpos.max(), span - 1)) + 1
+        n_cut = int(rng.integers(0, min(6, end - 1) + 1))
+        cut = np.sort(rng.choice(np.arange(1, end), n_cut, replace=False)) if n_cut else np.array([], int)
+        cu = np.concatenate([[0], cut, [end]]).astype(np.int32)
+    order = [int(c) for c in rng.permutation(n_chunks)]
+    _say("random ring", seed, dict(hq=hq, hkv=hkv, d=d, mask=mask, sq=sq, qsegs=qsegs, chunks=chunks,
+                                   order=order, docs=None if cu is None else len(cu) - 1))
+    a, scale = _attn(hq, hkv, d, mask, cu)
+    qb, q64 = _bf16(rng, (sq, hq, d))
+    dob, do64 = _bf16(rng, (sq, hq, d))
+    ks_b, ks_64, vs_b, vs_64 = [], [], [], []
+    for c in range(n_chunks):
+        n = sum(l for _, l in chunks[c])
+        kb, k64 = _bf16(rng, (n, hkv, d))
+        vb, v64 = _bf16(rng, (n, hkv, d))
+        ks_b.append(kb); ks_64.append(k64); vs_b.append(vb); vs_64.append(v64)
+    kpos_all = np.concatenate([np.concatenate([s + np.arange(l) for s, l in ch]) for ch in chunks])
+    k_all, v_all = np.concatenate(ks_64), np.concatenate(vs_64)
+    want_o, want_lse = oracle.attention(q64, k_all, v_all, qpos, kpos_all, mask, scale, cu)
+    wdq, wdk, wdv, _, _, _ = oracle.attention_backward(q64, k_all, v_all, do64, qpos, kpos_all, mask, scale, cu)
+
+    q, dO = to_device(qb, "bf16", DEV), to_device(dob, "bf16", DEV)
+    qs = rba.make_segs(qsegs)
+    kd = [to_device(x, "bf16", DEV) for x in ks_b]
+    vd = [to_device(x, "bf16", DEV) for x in vs_b]
+    kss = [rba.make_segs(ch) for ch in chunks]
+    o_acc = torch.zeros((sq, hq, d), device=DEV)
+    lse_acc = torch.full((hq, sq), float("-inf"), device=DEV)
+    for c in order:
+        rba.rba_fwd_step_acc(a, q, qs, kd[c], vd[c], kss[c], o_acc, lse_acc)
+    o_fin = torch.full((sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    rba.rba_merge(o_acc, lse_acc, None, None, o_fin, rba.RBA_BF16)
+    torch.cuda.synchronize()
+    assert_lse(lse_acc.cpu().numpy(), want_lse, "lse_acc")
+    assert_close(o_acc.cpu().numpy(), want_o, "bf16", "o_acc")
+    assert_close(o_fin.float().cpu().numpy(), want_o, "bf16", "o_final")
+
+    delta = torch.empty((hq, sq), device=DEV)
+    rba.rba_bwd_preprocess(o_acc, dO, delta)
+    dq = torch.zeros((sq, hq, d), device=DEV)
+    dk_parts, dv_parts = {}, {}
+    for c in order:
+        n = kd[c].shape[0]
+        dk = torch.zeros((n, hkv, d), device=DEV)
+        dv = torch.zeros((n, hkv, d), device=DEV)
+        rba.rba_bwd_step(a, q, qs, kd[c], vd[c], kss[c], dO, lse_acc, delta, dq, dk, dv)
+        dk_parts[c], dv_parts[c] = dk, dv
+    torch.cuda.synchronize()
+    got_dk = np.concatenate([dk_parts[c].cpu().numpy() for c in range(n_chunks)])
+    got_dv = np.concatenate([dv_parts[c].cpu().numpy() for c in range(n_chunks)])
+    # gradients at unit scale, as in test_random_backward_step
+    for name, got, want in (("dq", dq.cpu().numpy(), wdq), ("dk", got_dk, wdk), ("dv", got_dv, wdv)):
+        unit = max(1.0, float(np.sqrt(np.mean(want ** 2))))
+        assert_close(got / unit, want / unit, "bf16", name)
