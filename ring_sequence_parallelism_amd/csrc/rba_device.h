@@ -58,6 +58,10 @@ __device__ __forceinline__ DocLanes doc_lanes(const int32_t* cu, int32_t n_docs,
   DocLanes d;
   d.ok = cu != nullptr && n_docs > 0 && n_docs < 64;
   d.v = (d.ok && lane <= n_docs) ? cu[lane] : INT32_MAX;
+  // The lookups use the table at once; waiting here (vmcnt(0) alone) also
+  // tells the compiler that no load into it is pending on the paths that
+  // join this one, so code after them need not wait on vector memory.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   return d;
 }
 

@@ -71,20 +71,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.
   // Loaded first, so that the rest of the task setup runs while it lands.
+  // Lanes of rows past the chunk load row 0 (their results are never
+  // written): unconditional loads leave the load count the same on every
+  // path, so the setup's waits need not cover these loads.
   bf16x8 qreg[NQB][D / 16];
   {
     const int row0 = task_row0<QR>(p, th, wave), h = task_head_index(p, th, wave);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int row = row0 + qb * 32 + col;
-      const bool ok = row < p.sq;
       const bf16x8* src = reinterpret_cast<const bf16x8*>(
-          static_cast<const uint16_t*>(p.q) + ((size_t)(ok ? row : 0) * p.hq + h) * D);
+          static_cast<const uint16_t*>(p.q) + ((size_t)(row < p.sq ? row : 0) * p.hq + h) * D);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 z = {};
-        qreg[qb][ks] = ok ? src[2 * ks + half] : z;
-      }
+      for (int ks = 0; ks < D / 16; ++ks) qreg[qb][ks] = src[2 * ks + half];
     }
   }
   const WaveTask t = make_task_from<QR>(p, wave, th);
@@ -320,8 +319,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(FwdParams p) {
   constexpr int MAXI = 8;                          // items read per batch
   const int hg = blockIdx.x % p.n_head_groups;
   const int i = blockIdx.x / p.n_head_groups;      // order index, < n_split_rg
-  const int rg = p.order[i];
-  const int it0 = p.item_start[i], n_it = p.item_start[i + 1] - it0;
+  const int rg = karg_u16(p.order, i);
+  const int it0 = karg_u16(p.item_start, i), n_it = karg_u16(p.item_start, i + 1) - it0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = hg * p.hpw + wave % p.hpw;
   const int v0 = (lane & 7) * VPL;

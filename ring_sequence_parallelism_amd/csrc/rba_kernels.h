@@ -3,6 +3,8 @@
 // kernel needs about a chunk's positions travels in the kernel arguments.
 #pragma once
 
+#include <cstddef>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,10 +84,15 @@ struct FwdParams {
   int32_t n_active;
   int32_t n_split_rg;
   int32_t n_items;        // items of the n_active row groups
-  uint16_t item_start[kMaxSplitRg + 1];
+  uint16_t item_start[kMaxSplitRg + 2];   // one spare entry keeps split_len 4-byte aligned
   uint16_t split_len[kMaxSplitRg];   // tiles per item of each split row group (the last may have fewer)
   float* ws;              // workspace of the split items
 };
+
+// The 16-bit tables are read on the device as aligned 32-bit words.
+static_assert(offsetof(FwdParams, order) % 4 == 0 && offsetof(FwdParams, item_start) % 4 == 0 &&
+                  offsetof(FwdParams, split_len) % 4 == 0 && kMaxOrder % 2 == 0 && kMaxSplitRg % 2 == 0,
+              "16-bit kernel-argument tables must start and end on 4-byte boundaries");
 
 // Floats of one split item's workspace slot: the partial (O normalized, LSE)
 // of the 4 waves x 32 rows of a query-stationary workgroup.

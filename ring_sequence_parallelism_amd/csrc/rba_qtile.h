@@ -40,6 +40,14 @@ struct TaskHead {
   int skip, count, slot;
 };
 
+// Entry i of a 16-bit table in the kernel arguments, read as the aligned
+// 32-bit word that holds it: with a uniform index this is one scalar load,
+// where a 16-bit element read is a vector load and a wait on vector memory.
+__device__ __forceinline__ int karg_u16(const uint16_t* a, int i) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(a)[i >> 1];
+  return (int)((w >> ((i & 1) * 16)) & 0xffffu);
+}
+
 __device__ __forceinline__ TaskHead task_head(const FwdParams& p, int logical) {
   TaskHead t;
   t.skip = 0;
@@ -49,7 +57,7 @@ __device__ __forceinline__ TaskHead task_head(const FwdParams& p, int logical) {
   if (!p.split) {
     hg = logical / p.n_rg_launch;       // head group (query heads hg*hpw ...)
     const int rg_i = logical % p.n_rg_launch;
-    rg = p.n_order ? (int)p.order[rg_i]
+    rg = p.n_order ? karg_u16(p.order, rg_i)
                    : (p.order_reverse ? p.n_row_groups - 1 - rg_i : rg_i);   // heavy first when ordered
   } else {
     // per head group: the split items, the other active row groups, then
@@ -57,24 +65,24 @@ __device__ __forceinline__ TaskHead task_head(const FwdParams& p, int logical) {
     const int per_hg = p.n_items + p.n_row_groups - p.n_active;
     hg = logical / per_hg;
     const int it = logical % per_hg;
-    const int n_split_items = p.item_start[p.n_split_rg];
+    const int n_split_items = karg_u16(p.item_start, p.n_split_rg);
     int i;
     if (it < n_split_items) {
       int lo = 0, hi = p.n_split_rg - 1;   // the last i with item_start[i] <= it
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int)p.item_start[mid] <= it) lo = mid; else hi = mid - 1;
+        if (karg_u16(p.item_start, mid) <= it) lo = mid; else hi = mid - 1;
       }
       i = lo;
-      t.skip = (it - (int)p.item_start[i]) * (int)p.split_len[i];
-      t.count = p.split_len[i];
+      t.skip = (it - karg_u16(p.item_start, i)) * karg_u16(p.split_len, i);
+      t.count = karg_u16(p.split_len, i);
       t.slot = it * p.n_head_groups + hg;
     } else if (it < p.n_items) {
       i = p.n_split_rg + (it - n_split_items);
     } else {
       i = p.n_active + (it - p.n_items);
     }
-    rg = p.order[i];
+    rg = karg_u16(p.order, i);
   }
   t.hg = hg;
   t.rg = rg;
