@@ -63,10 +63,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int logical = xcd_remap(blockIdx.x, p.n_wg);
   // A merging step leaves the running result of rows that see no key as it
   // is (an empty partial merges as the identity): workgroups the host has
-  // listed after every row group with work end at once.
-  if (!p.split && (p.n_order || p.order_reverse) && p.accumulate && !p.o_final &&
-      logical % p.n_rg_launch >= p.n_active)
+  // listed after every row group with work end at once, or only convert
+  // that result when the final output is due.
+  if (!p.split && (p.n_order || p.order_reverse) && p.accumulate && logical % p.n_rg_launch >= p.n_active) {
+    if (p.o_final) copy_running_to_final<D, QR>(p, task_head(p, logical), wave, lane);
     return;
+  }
   const TaskHead th = task_head(p, logical);
 
   // Q^T as the B operand: lane holds query `col`, d = 16*ks + 8*half + 0..7.

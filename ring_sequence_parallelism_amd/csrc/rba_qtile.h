@@ -345,8 +345,10 @@ __device__ __forceinline__ void write_step_output(const FwdParams& p, int row, i
     return;
   }
   // An empty partial merges as the identity: the row's running result is
-  // neither read nor written (unless the final output is due).
-  if (lse == -INFINITY && !p.o_final) return;
+  // neither read nor written, and only read for the final output when that
+  // is due (the merge weights are then exactly 1 and 0).
+  const bool empty = lse == -INFINITY;
+  if (empty && !p.o_final) return;
   f32x4 old[D / 32][4];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -361,7 +363,7 @@ __device__ __forceinline__ void write_step_output(const FwdParams& p, int row, i
                           oacc[db][4 * jj + 3] * inv};
       const f32x4 o = w.wa * old[db][jj] + w.wb * part;
       const int c = db * 32 + 8 * jj + 4 * half;
-      *reinterpret_cast<f32x4*>(dst + c) = o;
+      if (!empty) *reinterpret_cast<f32x4*>(dst + c) = o;
       if (p.o_final) {
         if (p.final_bf16) {
           const u32x2 b = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -371,7 +373,32 @@ __device__ __forceinline__ void write_step_output(const FwdParams& p, int row, i
         }
       }
     }
-  if (half == 0) p.lse[li] = w.L;
+  if (half == 0 && !empty) p.lse[li] = w.L;
+}
+
+// The final output of a merging step's workgroup whose row group has no key
+// in the step: the running result unchanged (an empty partial merges as the
+// identity), converted.  Each wave copies its 32 rows of one head with
+// consecutive lanes on consecutive 16-byte pieces of a row.
+template <int D, int QR>
+__device__ __forceinline__ void copy_running_to_final(const FwdParams& p, const TaskHead& th, int wave, int lane) {
+  constexpr int CPR4 = D / 4;   // f32x4 pieces per row
+  static_assert(QR * CPR4 % 64 == 0, "whole passes of the wave");
+  const int row0 = task_row0<QR>(p, th, wave), h = task_head_index(p, th, wave);
+#pragma unroll 4
+  for (int i = 0; i < QR * CPR4 / 64; ++i) {
+    const int c = i * 64 + lane;
+    const int row = row0 + c / CPR4;
+    if (row >= p.sq) continue;
+    const size_t oi = ((size_t)row * p.hq + h) * D + 4 * (c % CPR4);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.o + oi);
+    if (p.final_bf16) {
+      const u32x2 b = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi) = b;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi) = o;
+    }
+  }
 }
 
 // Writes one lane's share of a split item's partial (O = oacc / l, the
