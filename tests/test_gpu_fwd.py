@@ -476,6 +476,46 @@ def test_fwd_step_acc_equals_step_plus_merge(final, d):
         assert (f2.float() == 7.0).all()
 
 
+@pytest.mark.parametrize("final", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_step_acc_final_rows_without_keys(final, d):
+    """A merging step that writes the final output, in which whole row groups
+    see no key: their final output is the running result converted (bit for
+    bit), their running result and LSE are left as they were, and the rest
+    matches rba_fwd_step followed by rba_merge."""
+    _say("fwd step acc final copy", d, final)
+    rng = np.random.default_rng(70 + d)
+    sq, sk, hq, hkv = 230, 180, 8, 2
+    qb, _ = _rand_inputs(rng, sq, hq, d, "bf16")
+    kb, _ = _rand_inputs(rng, sk, hkv, d, "bf16")
+    vb, _ = _rand_inputs(rng, sk, hkv, d, "bf16")
+    q, k, v = (to_device(x, "bf16", DEV) for x in (qb, kb, vb))
+    a = rba.attn_params(hq, hkv, d, float(np.float32(1 / np.sqrt(d))), rba.RBA_BF16, rba.RBA_MASK_CAUSAL)
+    qs, ks = rba.make_segs([(0, sq)]), rba.make_segs([(110, sk)])      # rows 0..109 see no key
+    acc0 = torch.from_numpy(rng.standard_normal((sq, hq, d)).astype(np.float32)).to(DEV)
+    lse0 = torch.from_numpy((rng.standard_normal((hq, sq)) * 2).astype(np.float32)).to(DEV)
+    lse0[1, 0:40] = float("-inf")
+    acc0[0:40, 1] = 0
+    fdt, tdt = (rba.RBA_BF16, torch.bfloat16) if final == "bf16" else (rba.RBA_F32, torch.float32)
+    o_part = torch.empty((sq, hq, d), device=DEV)
+    l_part = torch.empty((hq, sq), device=DEV)
+    assert rba.rba_fwd_step(a, q, qs, k, v, ks, o_part, l_part) == rba.RBA_OK
+    o_ref, l_ref = acc0.clone(), lse0.clone()
+    f_ref = torch.full((sq, hq, d), 7.0, dtype=tdt, device=DEV)
+    rba.rba_merge(o_ref, l_ref, o_part, l_part, f_ref, fdt)
+    o_acc, l_acc = acc0.clone(), lse0.clone()
+    f_acc = torch.full((sq, hq, d), 7.0, dtype=tdt, device=DEV)
+    assert rba.rba_fwd_step_acc(a, q, qs, k, v, ks, o_acc, l_acc, f_acc, fdt) == rba.RBA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o_acc[:110], acc0[:110]) and torch.equal(l_acc[:, :110], lse0[:, :110])
+    assert torch.equal(f_acc[:110], acc0[:110].to(tdt))
+    assert torch.allclose(o_acc, o_ref, rtol=2e-6, atol=2e-6)
+    fin = ~torch.isneginf(l_ref)
+    assert torch.equal(torch.isneginf(l_acc), torch.isneginf(l_ref))
+    assert torch.allclose(l_acc[fin], l_ref[fin], rtol=1e-6, atol=1e-6)
+    assert torch.allclose(f_acc.float(), f_ref.float(), rtol=1e-2 if final == "bf16" else 2e-6, atol=2e-6)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_replay_merge_paths_agree(fused):
     """The replay through rba_fwd_step_acc and through o_part + rba_merge both
