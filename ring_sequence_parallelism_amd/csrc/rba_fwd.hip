@@ -299,6 +299,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     const float lse = has ? m_run[qb] * kLn2 + __logf(l) : -INFINITY;
     if (t.slot >= 0)
       write_split_partial<D>(p, t.slot, wave, col, half, oacc[qb], inv, lse);
+    else if (p.accumulate && NQB == 1)
+      merge_step_output_coalesced<D>(p, t.row0 + qb * 32, t.h, lane, oacc[qb], inv, lse,
+                                     reinterpret_cast<float*>(&lds[0][0][0]) + wave * 32 * D);
     else
       write_step_output<D>(p, t.row0 + qb * 32 + col, t.h, half, oacc[qb], inv, lse);
   }

@@ -401,6 +401,81 @@ __device__ __forceinline__ void copy_running_to_final(const FwdParams& p, const 
   }
 }
 
+// The merging epilogue of one wave (32 rows of one head) with coalesced
+// global accesses.  Each lane scales its accumulator share by the partial's
+// merge weight (wb / l) into the wave's 32 x D fp32 block of LDS (16-byte
+// pieces XOR-swizzled by row); after a workgroup barrier lane l takes piece
+// l % 32 of rows 2 i + l / 32, i = 0..15: it loads the running output of
+// all 16 at once, then adds wa times each to the partial and stores the
+// merged rows (and the final output), each half-wave one whole row per
+// instruction.  A row whose partial is empty keeps its running output and
+// LSE untouched (weights exactly 1 and 0).  All four waves call it (it
+// holds two workgroup barriers); `w_lds` is the wave's LDS block.
+template <int D>
+__device__ __forceinline__ void merge_step_output_coalesced(const FwdParams& p, int row0, int h, int lane,
+                                                            const f32x16 (&oacc)[D / 32], float inv, float lse,
+                                                            float* w_lds) {
+  constexpr int P = D / 4;                  // 16-byte pieces per row
+  const int col = lane & 31, half = lane >> 5, q = lane & 31;
+  const int row = row0 + col;
+  const bool row_ok = row < p.sq;
+  const size_t li = (size_t)h * p.sq + (row_ok ? row : 0);
+  const float la = row_ok ? p.lse[li] : -INFINITY;
+  const bool empty = lse == -INFINITY;
+  const MergeWeights w = merge_weights(la, lse);
+  const float sb = w.wb * inv;
+  // per row, read by the other lanes through a shuffle: wa; -1 for a row
+  // that keeps its running result and writes nothing (and rows past the
+  // chunk); with the final output due and an empty partial, 2 (the running
+  // result is final as it is) or 3 (neither side has a key: zeros)
+  const float wa_row = (!row_ok || (empty && !p.o_final)) ? -1.f : (empty ? (la == -INFINITY ? 3.f : 2.f) : w.wa);
+  __syncthreads();   // every wave is done with the tile buffers
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int pc = db * 8 + 2 * jj + half;   // piece of d = 4 pc .. 4 pc + 3
+      const f32x4 v = {oacc[db][4 * jj] * sb, oacc[db][4 * jj + 1] * sb, oacc[db][4 * jj + 2] * sb,
+                       oacc[db][4 * jj + 3] * sb};
+      *reinterpret_cast<f32x4*>(w_lds + col * D + 4 * (pc ^ (col % P))) = v;
+    }
+  if (half == 0 && row_ok && !empty) p.lse[li] = w.L;
+  __syncthreads();
+  // every load first (rows past the chunk read its last row, unused), then
+  // the merge and the stores
+  float wa[16];
+  f32x4 old[16], part[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + half;
+    wa[i] = __shfl(wa_row, r);
+    const size_t oi = ((size_t)min(row0 + r, p.sq - 1) * p.hq + h) * D + 4 * min(q, P - 1);
+    old[i] = *reinterpret_cast<const f32x4*>(p.o + oi);
+    part[i] = *reinterpret_cast<const f32x4*>(w_lds + r * D + 4 * (min(q, P - 1) ^ (r % P)));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + half;
+    if (q >= P || wa[i] < 0.f) continue;
+    const size_t oi = ((size_t)(row0 + r) * p.hq + h) * D + 4 * q;
+    f32x4 o;
+    if (wa[i] > 1.5f) {
+      o = wa[i] > 2.5f ? f32x4{0.f, 0.f, 0.f, 0.f} : old[i];   // empty partial, final output due
+    } else {
+      o = wa[i] * old[i] + part[i];
+      *reinterpret_cast<f32x4*>(p.o + oi) = o;
+    }
+    if (p.o_final) {
+      if (p.final_bf16) {
+        const u32x2 b = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o_final) + oi) = b;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.o_final) + oi) = o;
+      }
+    }
+  }
+}
+
 // Writes one lane's share of a split item's partial (O = oacc / l, the
 // row's LSE) into its workspace slot: wave w's rows at floats
 // [w * 32 * D, (w + 1) * 32 * D) (row-major, D per row), their LSE at
