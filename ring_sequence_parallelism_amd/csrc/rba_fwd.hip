@@ -56,6 +56,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // [buffer][K, V] tiles, double-buffered: tile t is computed from buffer t % 2
   // while tile t + 1 streams into the other one.
   __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];
+  // the merging epilogue reuses the tile buffers: one 32-row fp32 block per wave
+  static_assert(kWaves * 32 * D * sizeof(float) <= sizeof(lds), "epilogue blocks fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: task setup stays scalar
