@@ -480,13 +480,46 @@ constexpr int64_t kSplitMaxBytes = int64_t(32) << 20;
 // launch (roughly the time of 8-10 such tiles), so shorter lists gain nothing.
 constexpr int64_t kSplitMinTiles = 32;
 
+// Fixed cost of a forward workgroup (setup, first tile, epilogue) and of the
+// split merge launch, in key-tile times, for the launch-length estimate.
+constexpr int64_t kWgFixedTiles = 4;
+constexpr int64_t kMergeTiles = 10;
+
+// Length of a forward launch in key-tile times, estimated by replaying the
+// hardware's dispatch: workgroups in logical order (per head group, `len`
+// holds the row groups' or items' tile counts in launch order), each XCD
+// taking a contiguous eighth of that order (xcd_remap) onto its share of the
+// slots, each workgroup starting on the slot that frees first.
+int64_t launch_length(const std::vector<int64_t>& len, int n_head_groups, int64_t slots) {
+  const int64_t n = (int64_t)len.size() * n_head_groups;
+  constexpr int64_t X = 8;
+  const int64_t per = n / X, rem = n % X, xslots = std::max<int64_t>(1, slots / X);
+  int64_t end = 0;
+  for (int64_t x = 0, base = 0; x < X; ++x) {
+    const int64_t cnt = per + (x < rem ? 1 : 0);
+    std::vector<int64_t> free_at(xslots, 0);
+    for (int64_t j = base; j < base + cnt; ++j) {
+      auto it = std::min_element(free_at.begin(), free_at.end());
+      *it += len[j % len.size()] + kWgFixedTiles;
+      end = std::max(end, *it);
+    }
+    base += cnt;
+  }
+  return end;
+}
+
 // Split plan of a forward launch (see FwdParams): when the row groups with
 // work give fewer workgroups than one round of the chip (two per compute
 // unit) and the heaviest visits at least kSplitMinTiles tiles, each heavy
 // row group's visit list is cut into items so that the launch has about one
 // round, each item at least 2 tiles; the items' partials then need
 // split_slot_floats(d) floats of workspace per item and head group, at most
-// `ws_limit` bytes (fewer, longer items otherwise).
+// `ws_limit` bytes (fewer, longer items otherwise).  When they give more
+// than one round but at most two, the heaviest row groups, as many as make
+// the rest fit one round, are cut in two halves, if the dispatch estimate
+// (launch_length) says the launch gets at least a tenth shorter, merge
+// launch included: a second round of whole row groups would otherwise run
+// on a few slots while the others wait.
 // Returns the workspace bytes the plan uses (0: no split, p unchanged).
 int64_t plan_split(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::FwdParams& p, int64_t ws_limit) {
   p.split = 0;
@@ -502,7 +535,8 @@ int64_t plan_split(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fwd
     n_active += tiles[rg].first > 0;
   }
   const int64_t slots = 2 * (int64_t)device_cus();
-  if (n_active == 0 || n_active * p.n_head_groups >= slots) return 0;
+  const int64_t H = p.n_head_groups;
+  if (n_active == 0 || n_active * H > 2 * slots) return 0;
   int64_t max_tiles = 0;
   for (const auto& t : tiles) max_tiles = std::max(max_tiles, t.first);
   if (max_tiles < kSplitMinTiles) return 0;
@@ -510,6 +544,34 @@ int64_t plan_split(const rba_attn* a, const StepPlan& plan, int64_t sq, rba::Fwd
     return x.first > y.first;
   });
   const int64_t slot_bytes = rba::split_slot_floats(a->d) * 4;
+  if (n_active * H >= slots) {
+    // a second round: halve the k heaviest so that the rest fit one round
+    const int64_t k = (n_active * H - slots + H - 1) / H;
+    if (k < 1 || k > n_active || k > rba::kMaxSplitRg) return 0;
+    std::vector<int64_t> whole, halved;
+    for (int i = 0; i < p.n_row_groups; ++i) whole.push_back(tiles[i].first);
+    for (int i = 0; i < k; ++i) {
+      halved.push_back((tiles[i].first + 1) / 2);
+      halved.push_back((tiles[i].first + 1) / 2);
+    }
+    for (int i = (int)k; i < p.n_row_groups; ++i) halved.push_back(tiles[i].first);
+    if (10 * (launch_length(halved, (int)H, slots) + kMergeTiles) > 9 * launch_length(whole, (int)H, slots))
+      return 0;
+    const int64_t bytes = 2 * k * H * slot_bytes;
+    if (bytes > std::min(ws_limit, kSplitMaxBytes)) return 0;
+    for (int i = 0; i < p.n_row_groups; ++i) p.order[i] = (uint16_t)tiles[i].second;
+    p.item_start[0] = 0;
+    for (int i = 0; i < k; ++i) {
+      p.split_len[i] = (uint16_t)((tiles[i].first + 1) / 2);
+      p.item_start[i + 1] = (uint16_t)(p.item_start[i] + 2);
+    }
+    p.split = 1;
+    p.n_active = (int32_t)n_active;
+    p.n_split_rg = (int32_t)k;
+    p.n_items = (int32_t)(2 * k + (n_active - k));
+    p.n_wg = (int32_t)(H * (p.n_items + p.n_row_groups - n_active));
+    return bytes;
+  }
   int64_t L = std::max<int64_t>(2, (total * p.n_head_groups + slots - 1) / slots);
   for (;; L *= 2) {
     int n_split = 0;

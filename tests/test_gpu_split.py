@@ -1,6 +1,8 @@
 """GPU parity of the forward step with a workspace (rba_fwd_step_ws), whose
 launches with few rows of work split each row group's key tiles over
-several workgroups and merge the items' partials in a second launch.
+several workgroups and merge the items' partials in a second launch (and
+launches of between one and two rounds of workgroups halve their heaviest
+row groups).
 
 Each case checks that the step does split (rba_fwd_workspace_size > 0),
 compares the result with the fp64 oracle at the forward's tolerances, and
@@ -57,6 +59,7 @@ SPLIT_CASES = [
     (96, 4096, 32, 8, 128, [(9000, 96)], [(0, 1000), (2000, 1500), (6000, 1596)], 1, None),   # items cross segments
     (150, 4096, 32, 8, 128, [(4096, 150)], [(0, 4096)], 2, [0, 700, 1000, 4180, 8192]),   # documents
     (33, 2048, 16, 4, 64, [(3000, 10, 7), (2100, 23)], [(0, 2048)], 1, None),   # strided query rows
+    (2432, 4096, 32, 8, 64, [(5000, 2432)], [(0, 4096)], 1, None),   # 608 workgroups: the 12 heaviest row groups halved
 ]
 
 
