@@ -400,6 +400,33 @@ def test_fwd_workspace_size_of_the_packed_document_steps():
     assert n.value == 0
 
 
+def test_fwd_workspace_size_split_regimes():
+    """The split planner's two regimes on steps whose tiles are all full
+    (queries after every key, causal; 32 q / 8 kv heads, so 8 head groups of
+    32-row workgroups, and 512 slots on a missing device's 256 compute
+    units): fewer workgroups than one round split (within the 32 MiB
+    workspace bound); 608 workgroups of 64
+    tiles (1.19 rounds) halve their 12 heaviest row groups, whose partials
+    take 2 x 12 x 8 slots of (4 x 32 x 128 + 128) floats; exactly two rounds,
+    more than two, or lists shorter than 32 tiles do not split."""
+    lib = rba.load()
+    a = rba.attn_params(32, 8, 128, 128 ** -0.5, rba.RBA_BF16, rba.RBA_MASK_CAUSAL)
+
+    def size(row_groups, sk):
+        n = ctypes.c_int64(-1)
+        qs, ks = rba.make_segs([(100000, 32 * row_groups)]), rba.make_segs([(0, sk)])
+        assert lib.rba_fwd_workspace_size(ctypes.byref(a), 32 * row_groups, ctypes.byref(qs), sk,
+                                          ctypes.byref(ks), ctypes.byref(n)) == rba.RBA_OK
+        return n.value
+
+    slot_bytes = (4 * 32 * 128 + 4 * 32) * 4
+    assert size(20, 4096) > 0                        # 160 workgroups: under one round
+    assert size(76, 4096) == 2 * 12 * 8 * slot_bytes  # 608 workgroups: 12 row groups halved
+    assert size(128, 4096) == 0                      # 1024 workgroups: two whole rounds
+    assert size(130, 4096) == 0                      # more than two rounds
+    assert size(76, 1024) == 0                       # 16 tiles per row group: too short
+
+
 def test_host_calls_from_several_threads():
     """The planner and the error string are per call / per thread: several
     host threads planning steps at once get each their own pair counts, and
